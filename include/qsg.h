@@ -1,0 +1,211 @@
+/*
+ * qsg.h - FP8 quantization and scaled FP8 GEMM for a transformer Linear
+ * layer, on AMD Instinct MI355X (gfx950).  C ABI of libqsg.so.
+ *
+ * What is computed (the pages that define it):
+ *   "Low-Precision Training Guide" (Megatron Core developer guide):
+ *     - section "Recipe Reference", recipes "delayed" (scale from a rolling
+ *       amax history), "tensorwise" (scale from the current tensor), "mxfp8"
+ *       (one power-of-two scale per 1x32 block) and "blockwise" (1x128
+ *       activation blocks with 128x128 weight blocks);
+ *     - table "Numerical Stability Knobs": --fp8-margin (M bits of headroom
+ *       in the scaling factor), --fp8-amax-history-len and
+ *       --fp8-amax-compute-algo;
+ *     - section "When to Use Low Precision": the FP8 GEMMs.
+ *   "How to reduce cuda memory usage of fp8?" (TransformerEngine issue 1764):
+ *     the backward pass of a Linear reads a transposed FP8 copy of its input,
+ *     hence the fused cast + transpose.
+ *   Outside the pages: the FP8 bit layouts of the OCP 8-bit floating point
+ *   specification (E4M3 max 448, E5M2 max 57344) and the E8M0 scale byte of
+ *   the OCP Microscaling v1.0 specification.
+ *
+ * Definitions used by every entry point:
+ *   enc(v)      saturating round-to-nearest-even FP8 encode of a binary32
+ *               value v: finite |v| >= max and +-inf give the signed max code
+ *               (0x7E / 0x7B), NaN gives sign|0x7F, the sign of zero is kept.
+ *   q = enc(fp32(x * scale))   one binary32 multiply (round to nearest even),
+ *               then enc.  bf16 inputs are widened to fp32 exactly first.
+ *   scale       fp32(fmax / amax) * 2^-margin; scale_inv = fp32(1 / scale).
+ *               amax == 0 or not finite gives scale = 1; a quotient that
+ *               overflows gives FLT_MAX.
+ *
+ * Conventions:
+ *   - Every pointer argument named *_dev or naming a tensor is a DEVICE
+ *     pointer (memory of the current HIP device).  The caller owns and
+ *     allocates every buffer; the library allocates and frees nothing.
+ *   - Matrices are row-major: element (r, c) of an R x C matrix with leading
+ *     dimension ld is at index r * ld + c.  Inputs take an explicit ld
+ *     (ld >= cols); FP8 and scale outputs are dense (ld = their column count).
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *     default stream), makes no host synchronisation and reads no device value
+ *     on the host, so a sequence of calls can be captured in a HIP graph.
+ *   - Return value: QSG_OK (0) or a negative qsg_status.  On error nothing
+ *     has been launched (argument errors) or a HIP launch error was seen
+ *     (QSG_ERR_HIP).  qsg_last_error() gives a message for the calling
+ *     thread's last error.
+ *   - Shapes with a zero dimension are valid and launch no work except where
+ *     a scalar output has to be written (amax = 0 and its scale).
+ */
+#ifndef QSG_H
+#define QSG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QSG_OK = 0,
+  QSG_ERR_ARG = -1,         /* null pointer, bad enum, negative size, ld < cols */
+  QSG_ERR_SHAPE = -2,       /* a shape rule of the recipe is violated */
+  QSG_ERR_ALIGN = -3,       /* a pointer is not aligned as the call requires */
+  QSG_ERR_UNSUPPORTED = -4, /* valid but unsupported combination */
+  QSG_ERR_HIP = -5          /* the HIP runtime reported an error */
+} qsg_status;
+
+/* FP8 formats ("Low-Precision Training Guide", table "Hardware and Recipe
+ * Compatibility": --fp8-format {e4m3, hybrid}; hybrid = E4M3 for forward
+ * tensors and E5M2 for gradients). */
+typedef enum { QSG_E4M3 = 0, QSG_E5M2 = 1 } qsg_fp8;
+
+/* Element types of high-precision inputs and of GEMM outputs. */
+typedef enum { QSG_F32 = 0, QSG_BF16 = 1 } qsg_dtype;
+
+/* Scaling recipes ("Low-Precision Training Guide", section "Recipe
+ * Reference").  For a GEMM operand this names the layout of its scales:
+ *   TENSORWISE, DELAYED  one fp32 scale_inv (device pointer to 1 float);
+ *   MXFP8                uint8 E8M0 bytes, rows x (K/32), byte = e + 127;
+ *   BLOCK_1X128          fp32 scale_inv, rows x (K/128);
+ *   BLOCK_128X128        fp32 scale_inv, ceil(rows/128) x (K/128). */
+typedef enum {
+  QSG_TENSORWISE = 0,
+  QSG_DELAYED = 1,
+  QSG_MXFP8 = 2,
+  QSG_BLOCK_1X128 = 3,
+  QSG_BLOCK_128X128 = 4
+} qsg_scaling;
+
+/* MXFP8 block-exponent rule.  CEIL (default): the smallest power of two
+ * 2^e with block_amax * 2^-e <= fmax, so no element saturates.
+ * OCP_FLOOR: e = floor(log2(block_amax)) - emax_elem (OCP MX v1.0), which
+ * can saturate elements. */
+typedef enum { QSG_MX_CEIL = 0, QSG_MX_OCP_FLOOR = 1 } qsg_mx_rule;
+
+/* amax-history reduction ("--fp8-amax-compute-algo"; only "max" is named). */
+typedef enum { QSG_AMAX_MAX = 0 } qsg_amax_algo;
+
+/* A recipe for qsg_quantize.  margin: integer in [0, 64]. */
+typedef struct {
+  int32_t scaling; /* qsg_scaling */
+  int32_t fmt;     /* qsg_fp8 */
+  int32_t margin;  /* --fp8-margin */
+  int32_t mx_rule; /* qsg_mx_rule, used by QSG_MXFP8 only */
+} qsg_recipe;
+
+/* Version of this ABI (major * 10000 + minor * 100 + patch). */
+int qsg_version(void);
+
+/* Text of a status code (static storage). */
+const char* qsg_status_string(int status);
+
+/* Message of the calling thread's last failing call (static per thread). */
+const char* qsg_last_error(void);
+
+/* Per-tensor amax ("Low-Precision Training Guide", recipe "tensorwise": the
+ * scale is computed from the current tensor).
+ *   x        rows x cols, dtype QSG_F32 or QSG_BF16, leading dimension ld;
+ *            16-byte aligned.
+ *   amax_dev out: 1 float, max |x| (-0 counts as 0; any NaN gives the NaN
+ *            0x7FC00000; an empty tensor gives 0).  Written on `stream`. */
+int qsg_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+             float* amax_dev, void* stream);
+
+/* Scale from an amax (recipe "tensorwise"; knob --fp8-margin).
+ *   amax_dev       in: 1 float.
+ *   scale_dev      out: 1 float, scale as defined above.
+ *   scale_inv_dev  out: 1 float, fp32(1/scale). */
+int qsg_compute_scale(const float* amax_dev, int fmt, int margin, float* scale_dev,
+                      float* scale_inv_dev, void* stream);
+
+/* Cast + transpose with a given per-tensor scale ("How to reduce cuda memory
+ * usage of fp8?": the transposed FP8 copy that backward reads; recipe
+ * "delayed": the amax of the raw tensor is recorded for the next step).
+ *   x             rows x cols (dtype, ld), 16-byte aligned.
+ *   scale_dev     in: 1 float.
+ *   q             out: rows x cols FP8 bytes, or NULL to skip.
+ *   qt            out: cols x rows FP8 bytes (qt[c*rows + r] = q[r*cols + c]),
+ *                 or NULL to skip.
+ *   amax_out_dev  out: 1 float, max |x| of this call (as qsg_amax), or NULL.
+ * Either output may be skipped; q and qt may not both be NULL. */
+int qsg_cast_transpose(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                       int fmt, const float* scale_dev, uint8_t* q, uint8_t* qt,
+                       float* amax_out_dev, void* stream);
+
+/* Delayed-scaling update ("Low-Precision Training Guide", recipe "delayed":
+ * the scaling factor comes from a rolling amax history; knobs
+ * --fp8-amax-history-len, --fp8-amax-compute-algo max, --fp8-margin).
+ *   history_dev   in/out: hist_len floats (hist_len >= 1); the caller zeroes
+ *                 it once before step 0.
+ *   step          host counter; amax is written into slot step mod hist_len.
+ *   amax_dev      in: 1 float (the amax of the tensor quantized at `step`).
+ *   scale_dev, scale_inv_dev  in/out: the scale in force; replaced by the
+ *                 scale of max(history), or left unchanged when that max is 0
+ *                 or not finite.  The caller sets them to 1 before step 0. */
+int qsg_amax_update(float* history_dev, int64_t hist_len, int64_t step,
+                    const float* amax_dev, int algo, int fmt, int margin,
+                    float* scale_dev, float* scale_inv_dev, void* stream);
+
+/* Quantize one tensor under a recipe, producing the row-wise copy (blocks run
+ * along cols, the GEMM contraction dimension of the tensor as stored) and/or
+ * the column-wise copy (blocks run along rows, stored transposed so that it
+ * is the row-wise quantization of x^T).
+ *
+ *   QSG_TENSORWISE  amax, scale and cast + transpose in one call.
+ *                   s  out: 3 floats {amax, scale, scale_inv}; st unused.
+ *   QSG_MXFP8       ("mxfp8": 1x32 blocks, power-of-two E8M0 scales)
+ *                   q  rows x cols, s  uint8 rows x (cols/32);   cols % 32 == 0
+ *                   qt cols x rows, st uint8 cols x (rows/32);   rows % 32 == 0
+ *   QSG_BLOCK_1X128 ("blockwise" activations)
+ *                   q  rows x cols, s  fp32 rows x (cols/128);   cols % 128 == 0
+ *                   qt cols x rows, st fp32 cols x (rows/128);   rows % 128 == 0
+ *   QSG_BLOCK_128X128 ("blockwise" weights)
+ *                   q  rows x cols, s  fp32 (rows/128) x (cols/128);
+ *                   qt = q^T, st = s^T;  rows % 128 == 0, cols % 128 == 0
+ * Scale tensors hold scale_inv (what the GEMM multiplies by) except MXFP8,
+ * which holds E8M0 bytes.  Pass NULL for (q, s) or (qt, st) to skip that
+ * copy.  QSG_DELAYED is not accepted here (use qsg_cast_transpose and
+ * qsg_amax_update). */
+int qsg_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                 const qsg_recipe* recipe, uint8_t* q, void* s, uint8_t* qt, void* st,
+                 void* stream);
+
+/* Scaled FP8 GEMM ("Low-Precision Training Guide", section "When to Use Low
+ * Precision": the FP8 GEMMs of a Linear; recipes "mxfp8" and "blockwise" for
+ * the scale granularity):
+ *
+ *     C[m, n] = sum_k (A[m, k] * sa(m, k)) * (B[n, k] * sb(n, k))
+ *
+ * A is M x K (lda), B is N x K (ldb): both K-contiguous FP8 bytes in formats
+ * fa / fb.  C is M x N (ldc) in c_dtype (QSG_BF16, rounded to nearest even,
+ * or QSG_F32), accumulated in fp32.  fprop, dgrad and wgrad all take this
+ * form by passing the transposed FP8 copies (dgrad: A = Q(dY), B = Q(W)^T;
+ * wgrad: A = Q(dY)^T, B = Q(X)^T).
+ * Scale kinds (ka, kb) and their pointers (see qsg_scaling):
+ *   (TENSORWISE|DELAYED, TENSORWISE|DELAYED)  1 float each
+ *   (MXFP8, MXFP8)                            K % 32 == 0
+ *   (BLOCK_1X128, BLOCK_128X128)              fprop / dgrad, K % 128 == 0
+ *   (BLOCK_1X128, BLOCK_1X128)                wgrad, K % 128 == 0
+ * Other pairs return QSG_ERR_UNSUPPORTED.  A, B, C must be 16-byte aligned;
+ * lda and ldb must be multiples of 16 and ldc a multiple of 8 elements for
+ * the vector path, otherwise a slower element-wise path is used. */
+int qsg_scaled_gemm(const uint8_t* a, int fa, int ka, const void* sa,
+                    const uint8_t* b, int fb, int kb, const void* sb,
+                    int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                    void* c, int c_dtype, int64_t ldc, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSG_H */

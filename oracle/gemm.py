@@ -1,0 +1,126 @@
+"""Scaled FP8 GEMM on dequantized operands, accumulated in fp64.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Every GEMM here computes ``C = (A * sa)(B * sb)^T`` with A stored M x K and B
+stored N x K (both K-contiguous), from the FP8 bytes and scales the quantizer
+produced ("Low-Precision Training Guide", section "When to Use Low Precision":
+the FP8 GEMMs; recipe sections "mxfp8" and "blockwise" for the scale
+granularity).  The three GEMMs of a Linear layer are all of this form:
+
+  fprop  Y  = X  W^T      A = Q(X)      M x K,  B = Q(W)      N x K
+  dgrad  dX = dY W        A = Q(dY)     M x N,  B = Q(W)^T    K x N
+  wgrad  dW = dY^T X      A = Q(dY)^T   N x M,  B = Q(X)^T    K x M
+
+The reference result is fp64 and is NOT rounded to the output dtype: the
+acceptance rule (``tolerance_check``) compares the GPU's bf16 / fp32 output
+against it.  ``gemm_exact_fraction`` is the same sum with exact rational
+arithmetic, for tiny shapes; the tests use it to pin the fp64 versions.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+
+from .fp8 import decode_exact, dequantize
+
+
+def gemm_per_tensor(qa, fa, sa_inv, qb, fb, sb_inv):
+    """Per-tensor scales (tensorwise and delayed recipes).
+
+    The decoded codes are summed first, then multiplied by sa_inv * sb_inv.
+    For E4M3 x E4M3 every product is a multiple of 2^-18 below 2^18, so the
+    fp64 sum is exact for K up to 2^17.
+    """
+    A = dequantize(qa, fa)
+    B = dequantize(qb, fb)
+    return (A @ B.T) * (np.float64(np.float32(sa_inv)) * np.float64(np.float32(sb_inv)))
+
+
+def _expand_blocks(s, rows, cols, br, bc):
+    """Broadcast a block-scale grid to a rows x cols array."""
+    s = np.asarray(s, dtype=np.float64)
+    return np.repeat(np.repeat(s, br, axis=0), bc, axis=1)[:rows, :cols]
+
+
+def gemm_mx(qa, fa, sa_e8m0, qb, fb, sb_e8m0):
+    """MXFP8: every 1 x 32 block along K is multiplied by 2^(byte - 127)."""
+    qa = np.asarray(qa)
+    qb = np.asarray(qb)
+    M, K = qa.shape
+    N = qb.shape[0]
+    ea = np.asarray(sa_e8m0, dtype=np.int64) - 127
+    eb = np.asarray(sb_e8m0, dtype=np.int64) - 127
+    A = dequantize(qa, fa) * _expand_blocks(np.ldexp(1.0, ea), M, K, 1, 32)
+    B = dequantize(qb, fb) * _expand_blocks(np.ldexp(1.0, eb), N, K, 1, 32)
+    return A @ B.T
+
+
+def gemm_block(qa, fa, sa_inv, qb, fb, sb_inv, b_blocks="128x128"):
+    """Blockwise: A has a 1 x 128 scale grid (M x K/128); B has either a
+    128 x 128 grid ((N/128) x (K/128), the weight of fprop and dgrad) or a
+    1 x 128 grid (N x K/128, the activation operand of wgrad)."""
+    qa = np.asarray(qa)
+    qb = np.asarray(qb)
+    M, K = qa.shape
+    N = qb.shape[0]
+    A = dequantize(qa, fa) * _expand_blocks(sa_inv, M, K, 1, 128)
+    if b_blocks == "128x128":
+        B = dequantize(qb, fb) * _expand_blocks(sb_inv, N, K, 128, 128)
+    elif b_blocks == "1x128":
+        B = dequantize(qb, fb) * _expand_blocks(sb_inv, N, K, 1, 128)
+    else:
+        raise ValueError(f"unknown block layout {b_blocks!r}")
+    return A @ B.T
+
+
+def gemm_exact_fraction(qa, fa, a_scale, qb, fb, b_scale):
+    """Exact rational GEMM for tiny shapes.
+
+    ``a_scale(m, k)`` and ``b_scale(n, k)`` return the exact (Fraction) scale
+    applied to element (m, k) of A and (n, k) of B.  Returns a list of lists
+    of Fractions.
+    """
+    qa = np.asarray(qa)
+    qb = np.asarray(qb)
+    M, K = qa.shape
+    N = qb.shape[0]
+    out = []
+    for m in range(M):
+        row = []
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                va = decode_exact(int(qa[m, k]), fa)
+                vb = decode_exact(int(qb[n, k]), fb)
+                acc += va * a_scale(m, k) * vb * b_scale(n, k)
+            row.append(acc)
+        out.append(row)
+    return out
+
+
+def tolerance_check(y, ref, rel=1e-2, floor=1e-3):
+    """Acceptance rule for GEMM outputs (reading of the 1e-2 relative
+    tolerance): every element must satisfy
+
+        |y - ref| <= rel * |ref| + floor * rms(ref).
+
+    The floor term absorbs binary32 accumulation-order error on sums that
+    cancel.  Returns (ok, info) where info holds the worst ratio, the
+    normwise relative error and how many elements pass only through the floor.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if y.shape != ref.shape:
+        raise ValueError(f"shape mismatch {y.shape} vs {ref.shape}")
+    if ref.size == 0:
+        return True, {"worst": 0.0, "normwise": 0.0, "floor_only": 0}
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    err = np.abs(y - ref)
+    bound = rel * np.abs(ref) + floor * rms
+    ok = bool(np.all(err <= bound))
+    worst = float(np.max(err / np.where(bound > 0, bound, 1.0)))
+    nrm = float(np.linalg.norm(ref))
+    normwise = float(np.linalg.norm(y - ref) / nrm) if nrm > 0 else float(np.linalg.norm(y - ref))
+    floor_only = int(np.sum((err > rel * np.abs(ref)) & (err <= bound)))
+    return ok, {"worst": worst, "normwise": normwise, "floor_only": floor_only}

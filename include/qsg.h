@@ -115,7 +115,8 @@ const char* qsg_last_error(void);
 /* Per-tensor amax ("Low-Precision Training Guide", recipe "tensorwise": the
  * scale is computed from the current tensor).
  *   x        rows x cols, dtype QSG_F32 or QSG_BF16, leading dimension ld;
- *            16-byte aligned.
+ *            aligned to its element size (16-byte alignment of x and of
+ *            ld * element size selects the vector path).
  *   amax_dev out: 1 float, max |x| (-0 counts as 0; any NaN gives the NaN
  *            0x7FC00000; an empty tensor gives 0).  Written on `stream`. */
 int qsg_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
@@ -131,13 +132,17 @@ int qsg_compute_scale(const float* amax_dev, int fmt, int margin, float* scale_d
 /* Cast + transpose with a given per-tensor scale ("How to reduce cuda memory
  * usage of fp8?": the transposed FP8 copy that backward reads; recipe
  * "delayed": the amax of the raw tensor is recorded for the next step).
- *   x             rows x cols (dtype, ld), 16-byte aligned.
+ *   x             rows x cols (dtype, ld), aligned to its element size; the
+ *                 vector path needs x and ld * element size 16-byte aligned,
+ *                 q 8-byte aligned with cols % 8 == 0, qt 16-byte aligned with
+ *                 rows % 16 == 0; otherwise an element-wise path is used.
  *   scale_dev     in: 1 float.
  *   q             out: rows x cols FP8 bytes, or NULL to skip.
  *   qt            out: cols x rows FP8 bytes (qt[c*rows + r] = q[r*cols + c]),
  *                 or NULL to skip.
  *   amax_out_dev  out: 1 float, max |x| of this call (as qsg_amax), or NULL.
- * Either output may be skipped; q and qt may not both be NULL. */
+ * Either output may be skipped; q and qt may not both be NULL unless the
+ * tensor is empty. */
 int qsg_cast_transpose(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                        int fmt, const float* scale_dev, uint8_t* q, uint8_t* qt,
                        float* amax_out_dev, void* stream);
@@ -196,9 +201,11 @@ int qsg_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
  *   (MXFP8, MXFP8)                            K % 32 == 0
  *   (BLOCK_1X128, BLOCK_128X128)              fprop / dgrad, K % 128 == 0
  *   (BLOCK_1X128, BLOCK_1X128)                wgrad, K % 128 == 0
- * Other pairs return QSG_ERR_UNSUPPORTED.  A, B, C must be 16-byte aligned;
- * lda and ldb must be multiples of 16 and ldc a multiple of 8 elements for
- * the vector path, otherwise a slower element-wise path is used. */
+ * Other pairs return QSG_ERR_UNSUPPORTED.  C must be aligned to its element
+ * size.  The vector path needs A and B 16-byte aligned with lda and ldb
+ * multiples of 16 (else A and B are read byte by byte), and C 8-byte (bf16)
+ * or 16-byte (fp32) aligned with ldc a multiple of 4 (else C is written
+ * element by element). */
 int qsg_scaled_gemm(const uint8_t* a, int fa, int ka, const void* sa,
                     const uint8_t* b, int fb, int kb, const void* sb,
                     int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,

@@ -1,0 +1,181 @@
+"""Python binding of libqsg.so (FP8 quantization and scaled FP8 GEMM on
+MI355X / gfx950).
+
+Argument marshalling only: every function below has the name of the C entry
+point it calls (declared in include/qsg.h), turns torch tensors into device
+pointers, sizes and leading dimensions, passes the current HIP stream, and
+raises ``QsgError`` on a non-zero status.  All computation happens in the HIP
+kernels of the library.  There is no fallback: if the library is missing or
+fails to load, every call raises.
+"""
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libqsg.so")
+
+# enums of include/qsg.h
+E4M3, E5M2 = 0, 1
+F32, BF16 = 0, 1
+TENSORWISE, DELAYED, MXFP8, BLOCK_1X128, BLOCK_128X128 = 0, 1, 2, 3, 4
+MX_CEIL, MX_OCP_FLOOR = 0, 1
+AMAX_MAX = 0
+
+FMT = {"e4m3": E4M3, "e5m2": E5M2}
+
+ENTRY_POINTS = (
+    "qsg_version",
+    "qsg_status_string",
+    "qsg_last_error",
+    "qsg_amax",
+    "qsg_compute_scale",
+    "qsg_cast_transpose",
+    "qsg_amax_update",
+    "qsg_quantize",
+    "qsg_scaled_gemm",
+)
+
+
+class QsgError(RuntimeError):
+    pass
+
+
+class Recipe(ctypes.Structure):
+    _fields_ = [("scaling", ctypes.c_int32), ("fmt", ctypes.c_int32),
+                ("margin", ctypes.c_int32), ("mx_rule", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libqsg.so (once) and declare the argument types."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise QsgError(f"{path} is not built: run `python -m quantize_scaled_gemm_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I, I64, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+    lib.qsg_version.restype = I
+    lib.qsg_version.argtypes = []
+    lib.qsg_status_string.restype = ctypes.c_char_p
+    lib.qsg_status_string.argtypes = [I]
+    lib.qsg_last_error.restype = ctypes.c_char_p
+    lib.qsg_last_error.argtypes = []
+    lib.qsg_amax.restype = I
+    lib.qsg_amax.argtypes = [P, I, I64, I64, I64, F, P]
+    lib.qsg_compute_scale.restype = I
+    lib.qsg_compute_scale.argtypes = [F, I, I, F, F, P]
+    lib.qsg_cast_transpose.restype = I
+    lib.qsg_cast_transpose.argtypes = [P, I, I64, I64, I64, I, F, P, P, F, P]
+    lib.qsg_amax_update.restype = I
+    lib.qsg_amax_update.argtypes = [F, I64, I64, F, I, I, I, F, F, P]
+    lib.qsg_quantize.restype = I
+    lib.qsg_quantize.argtypes = [P, I, I64, I64, I64, ctypes.POINTER(Recipe), P, P, P, P, P]
+    lib.qsg_scaled_gemm.restype = I
+    lib.qsg_scaled_gemm.argtypes = [P, I, I, P, P, I, I, P, I64, I64, I64, I64, I64, P, I, I64, P]
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise QsgError("tensors passed to libqsg must live on the GPU")
+    return t.data_ptr()
+
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise QsgError(f"unsupported input dtype {t.dtype}")
+
+
+def _matrix(t):
+    """(rows, cols, ld) of a 2-D row-major tensor view (unit column stride)."""
+    if t.dim() != 2:
+        raise QsgError("expected a 2-D tensor")
+    rows, cols = t.shape
+    if t.numel() == 0:
+        return rows, cols, max(cols, 1)
+    if cols > 1 and t.stride(1) != 1:
+        raise QsgError("the last dimension must be contiguous")
+    ld = t.stride(0) if rows > 1 else max(cols, 1)
+    return rows, cols, max(ld, cols)
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(rc):
+    if rc != 0:
+        lib = load_library()
+        msg = lib.qsg_last_error().decode()
+        raise QsgError(f"{lib.qsg_status_string(rc).decode()} ({rc}): {msg}")
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def qsg_version():
+    return load_library().qsg_version()
+
+
+def qsg_amax(x, amax, stream=None):
+    """amax (1 fp32 on the GPU) = max |x|."""
+    rows, cols, ld = _matrix(x)
+    _check(load_library().qsg_amax(_ptr(x), _dtype_code(x), rows, cols, ld, _ptr(amax), _stream(stream)))
+
+
+def qsg_compute_scale(amax, fmt, margin, scale, scale_inv, stream=None):
+    _check(load_library().qsg_compute_scale(_ptr(amax), fmt, margin, _ptr(scale), _ptr(scale_inv),
+                                            _stream(stream)))
+
+
+def qsg_cast_transpose(x, fmt, scale, q=None, qt=None, amax_out=None, stream=None):
+    rows, cols, ld = _matrix(x)
+    _check(load_library().qsg_cast_transpose(_ptr(x), _dtype_code(x), rows, cols, ld, fmt, _ptr(scale),
+                                             _ptr(q), _ptr(qt), _ptr(amax_out), _stream(stream)))
+
+
+def qsg_amax_update(history, step, amax, fmt, margin, scale, scale_inv, algo=AMAX_MAX, stream=None):
+    _check(load_library().qsg_amax_update(_ptr(history), history.numel(), step, _ptr(amax), algo, fmt,
+                                          margin, _ptr(scale), _ptr(scale_inv), _stream(stream)))
+
+
+def qsg_quantize(x, scaling, fmt, q=None, s=None, qt=None, st=None, margin=0, mx_rule=MX_CEIL,
+                 stream=None):
+    rows, cols, ld = _matrix(x)
+    rec = Recipe(scaling, fmt, margin, mx_rule)
+    _check(load_library().qsg_quantize(_ptr(x), _dtype_code(x), rows, cols, ld, ctypes.byref(rec),
+                                       _ptr(q), _ptr(s), _ptr(qt), _ptr(st), _stream(stream)))
+
+
+def qsg_scaled_gemm(a, fa, ka, sa, b, fb, kb, sb, c, stream=None):
+    """C (M x N) = (A sa)(B sb)^T; A is M x K and B is N x K (uint8 FP8 bytes)."""
+    M, K, lda = _matrix(a)
+    N, Kb, ldb = _matrix(b)
+    if Kb != K:
+        raise QsgError(f"K mismatch: A has {K}, B has {Kb}")
+    Mc, Nc, ldc = _matrix(c)
+    if (Mc, Nc) != (M, N):
+        raise QsgError(f"C is {Mc}x{Nc}, expected {M}x{N}")
+    _check(load_library().qsg_scaled_gemm(_ptr(a), fa, ka, _ptr(sa), _ptr(b), fb, kb, _ptr(sb), M, N, K,
+                                          lda, ldb, _ptr(c), _dtype_code(c), ldc, _stream(stream)))

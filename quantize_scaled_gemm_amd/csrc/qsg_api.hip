@@ -1,0 +1,197 @@
+// C ABI of libqsg.so (declared in include/qsg.h): argument validation, then
+// the launchers.  No exception crosses this boundary; nothing here allocates
+// device memory or synchronises with the device.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "qsg.h"
+#include "qsg_internal.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(QSG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return QSG_OK;
+}
+
+bool valid_fmt(int f) { return f == QSG_E4M3 || f == QSG_E5M2; }
+bool valid_dtype(int d) { return d == QSG_F32 || d == QSG_BF16; }
+int esize(int dtype) { return dtype == QSG_BF16 ? 2 : 4; }
+bool aligned(const void* p, int n) { return ((uintptr_t)p % (uintptr_t)n) == 0; }
+
+int check_matrix(const char* fn, const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld) {
+  if (!valid_dtype(dtype)) return fail(QSG_ERR_ARG, "%s: bad dtype %d", fn, dtype);
+  if (rows < 0 || cols < 0) return fail(QSG_ERR_ARG, "%s: negative shape %lld x %lld", fn, (long long)rows, (long long)cols);
+  if (rows > 0 && cols > 0) {
+    if (!x) return fail(QSG_ERR_ARG, "%s: null input", fn);
+    if (ld < cols) return fail(QSG_ERR_ARG, "%s: ld %lld < cols %lld", fn, (long long)ld, (long long)cols);
+    if (!aligned(x, esize(dtype))) return fail(QSG_ERR_ALIGN, "%s: input not aligned to its element size", fn);
+  }
+  return QSG_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int qsg_version(void) { return 100; }
+
+const char* qsg_status_string(int status) {
+  switch (status) {
+    case QSG_OK: return "ok";
+    case QSG_ERR_ARG: return "invalid argument";
+    case QSG_ERR_SHAPE: return "shape not allowed by the recipe";
+    case QSG_ERR_ALIGN: return "misaligned pointer";
+    case QSG_ERR_UNSUPPORTED: return "unsupported combination";
+    case QSG_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* qsg_last_error(void) { return g_msg; }
+
+int qsg_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, float* amax_dev,
+             void* stream) {
+  int rc = check_matrix("qsg_amax", x, dtype, rows, cols, ld);
+  if (rc) return rc;
+  if (!amax_dev) return fail(QSG_ERR_ARG, "qsg_amax: null amax");
+  if (!aligned(amax_dev, 4)) return fail(QSG_ERR_ALIGN, "qsg_amax: amax not 4-byte aligned");
+  qsg::launch_amax(x, dtype, rows, cols, ld, amax_dev, as_stream(stream));
+  return check_launch("qsg_amax");
+}
+
+int qsg_compute_scale(const float* amax_dev, int fmt, int margin, float* scale_dev,
+                      float* scale_inv_dev, void* stream) {
+  if (!amax_dev || !scale_dev || !scale_inv_dev) return fail(QSG_ERR_ARG, "qsg_compute_scale: null pointer");
+  if (!valid_fmt(fmt)) return fail(QSG_ERR_ARG, "qsg_compute_scale: bad fmt %d", fmt);
+  if (margin < 0 || margin > 64) return fail(QSG_ERR_ARG, "qsg_compute_scale: margin %d outside [0, 64]", margin);
+  qsg::launch_compute_scale(amax_dev, fmt, margin, scale_dev, scale_inv_dev, as_stream(stream));
+  return check_launch("qsg_compute_scale");
+}
+
+int qsg_cast_transpose(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt,
+                       const float* scale_dev, uint8_t* q, uint8_t* qt, float* amax_out_dev,
+                       void* stream) {
+  int rc = check_matrix("qsg_cast_transpose", x, dtype, rows, cols, ld);
+  if (rc) return rc;
+  if (!valid_fmt(fmt)) return fail(QSG_ERR_ARG, "qsg_cast_transpose: bad fmt %d", fmt);
+  if (!scale_dev) return fail(QSG_ERR_ARG, "qsg_cast_transpose: null scale");
+  const bool empty = rows == 0 || cols == 0;
+  if (!q && !qt && !empty) return fail(QSG_ERR_ARG, "qsg_cast_transpose: q and qt are both null");
+  if (amax_out_dev && !aligned(amax_out_dev, 4)) return fail(QSG_ERR_ALIGN, "qsg_cast_transpose: amax_out not aligned");
+  qsg::launch_cast_transpose(x, dtype, rows, cols, ld, fmt, scale_dev, q, qt, amax_out_dev, as_stream(stream));
+  return check_launch("qsg_cast_transpose");
+}
+
+int qsg_amax_update(float* history_dev, int64_t hist_len, int64_t step, const float* amax_dev,
+                    int algo, int fmt, int margin, float* scale_dev, float* scale_inv_dev,
+                    void* stream) {
+  if (!history_dev || !amax_dev || !scale_dev || !scale_inv_dev) return fail(QSG_ERR_ARG, "qsg_amax_update: null pointer");
+  if (hist_len < 1) return fail(QSG_ERR_ARG, "qsg_amax_update: hist_len %lld < 1", (long long)hist_len);
+  if (step < 0) return fail(QSG_ERR_ARG, "qsg_amax_update: negative step");
+  if (algo != QSG_AMAX_MAX) return fail(QSG_ERR_UNSUPPORTED, "qsg_amax_update: only the max algorithm is defined");
+  if (!valid_fmt(fmt)) return fail(QSG_ERR_ARG, "qsg_amax_update: bad fmt %d", fmt);
+  if (margin < 0 || margin > 64) return fail(QSG_ERR_ARG, "qsg_amax_update: margin %d outside [0, 64]", margin);
+  qsg::launch_amax_update(history_dev, hist_len, step, amax_dev, fmt, margin, scale_dev, scale_inv_dev,
+                          as_stream(stream));
+  return check_launch("qsg_amax_update");
+}
+
+int qsg_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                 const qsg_recipe* recipe, uint8_t* q, void* s, uint8_t* qt, void* st, void* stream) {
+  const char* fn = "qsg_quantize";
+  int rc = check_matrix(fn, x, dtype, rows, cols, ld);
+  if (rc) return rc;
+  if (!recipe) return fail(QSG_ERR_ARG, "%s: null recipe", fn);
+  const int scaling = recipe->scaling, fmt = recipe->fmt, margin = recipe->margin;
+  if (!valid_fmt(fmt)) return fail(QSG_ERR_ARG, "%s: bad fmt %d", fn, fmt);
+  if (margin < 0 || margin > 64) return fail(QSG_ERR_ARG, "%s: margin %d outside [0, 64]", fn, margin);
+  hipStream_t hs = as_stream(stream);
+  if (scaling == QSG_TENSORWISE) {
+    if (!s) return fail(QSG_ERR_ARG, "%s: tensorwise needs s = {amax, scale, scale_inv}", fn);
+    if (!q && !qt && rows > 0 && cols > 0) return fail(QSG_ERR_ARG, "%s: q and qt are both null", fn);
+    if (!aligned(s, 4)) return fail(QSG_ERR_ALIGN, "%s: s not aligned", fn);
+    float* f = reinterpret_cast<float*>(s);
+    qsg::launch_amax(x, dtype, rows, cols, ld, f, hs);
+    qsg::launch_compute_scale(f, fmt, margin, f + 1, f + 2, hs);
+    qsg::launch_cast_transpose(x, dtype, rows, cols, ld, fmt, f + 1, q, qt, nullptr, hs);
+    return check_launch(fn);
+  }
+  if (scaling == QSG_DELAYED)
+    return fail(QSG_ERR_UNSUPPORTED, "%s: delayed scaling uses qsg_cast_transpose + qsg_amax_update", fn);
+  if (scaling != QSG_MXFP8 && scaling != QSG_BLOCK_1X128 && scaling != QSG_BLOCK_128X128)
+    return fail(QSG_ERR_ARG, "%s: bad scaling %d", fn, scaling);
+  if (scaling == QSG_MXFP8 && recipe->mx_rule != QSG_MX_CEIL && recipe->mx_rule != QSG_MX_OCP_FLOOR)
+    return fail(QSG_ERR_ARG, "%s: bad mx_rule %d", fn, recipe->mx_rule);
+  if (rows == 0 || cols == 0) return QSG_OK;  // nothing to quantize, no scale to write
+  const bool row = q != nullptr, col = qt != nullptr;
+  if (!row && !col) return fail(QSG_ERR_ARG, "%s: q and qt are both null", fn);
+  if ((row && !s) || (col && !st)) return fail(QSG_ERR_ARG, "%s: a requested copy has a null scale tensor", fn);
+  if (scaling != QSG_MXFP8) {
+    if ((s && !aligned(s, 4)) || (st && !aligned(st, 4))) return fail(QSG_ERR_ALIGN, "%s: fp32 scales not aligned", fn);
+  }
+  const int64_t B = scaling == QSG_MXFP8 ? 32 : 128;
+  if (scaling == QSG_BLOCK_128X128) {
+    if (rows % 128 || cols % 128)
+      return fail(QSG_ERR_SHAPE, "%s: 128x128 blocks need rows and cols multiples of 128 (%lld x %lld)", fn,
+                  (long long)rows, (long long)cols);
+  } else {
+    if (row && cols % B)
+      return fail(QSG_ERR_SHAPE, "%s: row-wise blocks need cols %% %lld == 0 (cols %lld)", fn, (long long)B, (long long)cols);
+    if (col && rows % B)
+      return fail(QSG_ERR_SHAPE, "%s: column-wise blocks need rows %% %lld == 0 (rows %lld)", fn, (long long)B, (long long)rows);
+  }
+  qsg::launch_quantize_blocked(x, dtype, rows, cols, ld, scaling, fmt, margin,
+                               recipe->mx_rule == QSG_MX_CEIL, q, s, qt, st, hs);
+  return check_launch(fn);
+}
+
+int qsg_scaled_gemm(const uint8_t* a, int fa, int ka, const void* sa, const uint8_t* b, int fb,
+                    int kb, const void* sb, int64_t M, int64_t N, int64_t K, int64_t lda,
+                    int64_t ldb, void* c, int c_dtype, int64_t ldc, void* stream) {
+  const char* fn = "qsg_scaled_gemm";
+  if (!valid_fmt(fa) || !valid_fmt(fb)) return fail(QSG_ERR_ARG, "%s: bad fp8 format", fn);
+  if (!valid_dtype(c_dtype)) return fail(QSG_ERR_ARG, "%s: bad output dtype", fn);
+  if (M < 0 || N < 0 || K < 0) return fail(QSG_ERR_ARG, "%s: negative shape", fn);
+  const bool pt_a = ka == QSG_TENSORWISE || ka == QSG_DELAYED;
+  const bool pt_b = kb == QSG_TENSORWISE || kb == QSG_DELAYED;
+  int mode;
+  if (pt_a && pt_b) mode = 0;
+  else if (ka == QSG_MXFP8 && kb == QSG_MXFP8) mode = 1;
+  else if (ka == QSG_BLOCK_1X128 && kb == QSG_BLOCK_128X128) mode = 2;
+  else if (ka == QSG_BLOCK_1X128 && kb == QSG_BLOCK_1X128) mode = 3;
+  else {
+    const bool known = (ka >= 0 && ka <= 4) && (kb >= 0 && kb <= 4);
+    return fail(known ? QSG_ERR_UNSUPPORTED : QSG_ERR_ARG, "%s: scale kinds (%d, %d) not supported", fn, ka, kb);
+  }
+  if (mode == 1 && K % 32) return fail(QSG_ERR_SHAPE, "%s: MXFP8 needs K %% 32 == 0 (K %lld)", fn, (long long)K);
+  if ((mode == 2 || mode == 3) && K % 128) return fail(QSG_ERR_SHAPE, "%s: blockwise needs K %% 128 == 0 (K %lld)", fn, (long long)K);
+  if (M == 0 || N == 0) return QSG_OK;
+  if (!c) return fail(QSG_ERR_ARG, "%s: null C", fn);
+  if (ldc < N) return fail(QSG_ERR_ARG, "%s: ldc < N", fn);
+  if (!aligned(c, c_dtype == QSG_BF16 ? 2 : 4)) return fail(QSG_ERR_ALIGN, "%s: C not aligned to its element size", fn);
+  if (K > 0) {
+    if (!a || !b) return fail(QSG_ERR_ARG, "%s: null operand", fn);
+    if (lda < K || ldb < K) return fail(QSG_ERR_ARG, "%s: lda/ldb < K", fn);
+  }
+  if (!sa || !sb) return fail(QSG_ERR_ARG, "%s: null scale", fn);
+  if (mode != 1 && (!aligned(sa, 4) || !aligned(sb, 4))) return fail(QSG_ERR_ALIGN, "%s: fp32 scales not aligned", fn);
+  qsg::launch_scaled_gemm(a, fa, ka, sa, b, fb, kb, sb, M, N, K, lda, ldb, c, c_dtype, ldc, as_stream(stream));
+  return check_launch(fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,157 @@
+// Device helpers shared by the gfx950 kernels: FP8 encoding, bit tricks,
+// wavefront reductions.
+//
+// FP8 formats: OCP 8-bit floating point (E4M3 max 448, E5M2 max 57344), as
+// named by the "--fp8-format {e4m3,hybrid}" flag of the "Low-Precision
+// Training Guide".  Encoding is saturating round-to-nearest-even: finite
+// overflow and infinities clamp to the signed maximum, NaN gives sign|0x7F.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsg {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (read once: non-temporal hint).
+__device__ __forceinline__ u32x4 ld_stream16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+constexpr int kE4M3 = 0;
+constexpr int kE5M2 = 1;
+
+template <int FMT>
+struct Fp8Traits;
+template <>
+struct Fp8Traits<kE4M3> {
+  static constexpr float kMax = 448.0f;
+  static constexpr int kEmaxElem = 8;  // 448 = 1.75 * 2^8
+};
+template <>
+struct Fp8Traits<kE5M2> {
+  static constexpr float kMax = 57344.0f;
+  static constexpr int kEmaxElem = 15;  // 57344 = 1.75 * 2^15
+};
+
+__host__ __device__ inline float fp8_max(int fmt) { return fmt == kE4M3 ? 448.0f : 57344.0f; }
+
+// Convert two binary32 values to FP8 and place the two codes in the low
+// (HI=false) or high (HI=true) 16 bits of `old`.  The hardware conversion
+// rounds to nearest even; the med3 clamp makes it saturating for finite
+// values and infinities.  NaN inputs are patched to sign|0x7F afterwards so
+// the result does not depend on how the clamp and the conversion treat NaN.
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t cvt_pk(float a, float b, uint32_t old) {
+  constexpr float m = Fp8Traits<FMT>::kMax;
+  float ca = __builtin_amdgcn_fmed3f(a, -m, m);
+  float cb = __builtin_amdgcn_fmed3f(b, -m, m);
+  uint32_t r;
+  if constexpr (FMT == kE4M3)
+    r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, (int)old, HI);
+  else
+    r = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(ca, cb, (int)old, HI);
+  if (__builtin_expect(__builtin_isnan(a) | __builtin_isnan(b), 0)) {
+    const int sh = HI ? 16 : 0;
+    if (__builtin_isnan(a)) {
+      uint32_t code = ((__float_as_uint(a) >> 24) & 0x80u) | 0x7Fu;
+      r = (r & ~(0xFFu << sh)) | (code << sh);
+    }
+    if (__builtin_isnan(b)) {
+      uint32_t code = ((__float_as_uint(b) >> 24) & 0x80u) | 0x7Fu;
+      r = (r & ~(0xFF00u << sh)) | (code << (sh + 8));
+    }
+  }
+  return r;
+}
+
+// Four binary32 values -> four FP8 codes packed little-endian in a dword.
+template <int FMT>
+__device__ __forceinline__ uint32_t enc4(float a, float b, float c, float d) {
+  uint32_t lo = cvt_pk<FMT, false>(a, b, 0u);
+  return cvt_pk<FMT, true>(c, d, lo);
+}
+
+// bf16 <-> fp32 (exact widening; RNE narrowing of finite values, NaN kept quiet).
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// |x| of a binary32 bit pattern; NaNs become the canonical 0x7FC00000 so
+// that an integer max over |x| patterns is order-free and reports NaN as
+// 0x7FC00000 (NaN > +inf > finite as unsigned integers).
+__device__ __forceinline__ uint32_t abs_bits_canon(uint32_t u) {
+  u &= 0x7FFFFFFFu;
+  return u > 0x7F800000u ? 0x7FC00000u : u;
+}
+
+// Wavefront (64 lanes) unsigned max via DPP/permute-free shuffles.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+// Max over lanes that differ only in the bits of MASK_BITS (xor pattern).
+template <int MASK>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    if (MASK & off) {
+      uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
+      v = v > o ? v : o;
+    }
+  }
+  return v;
+}
+
+// Per-tensor scale (recipe "tensorwise" and the --fp8-margin knob of the
+// "Low-Precision Training Guide"): scale = fp32(fmax / amax) * 2^-margin,
+// with amax == 0 or non-finite giving 1 and an overflowing quotient giving
+// FLT_MAX.  The division is the IEEE correctly rounded one.
+__device__ __forceinline__ float scale_from_amax(float amax, float fmax, int margin) {
+  uint32_t ab = __float_as_uint(amax) & 0x7FFFFFFFu;
+  if (ab == 0u || ab >= 0x7F800000u) return 1.0f;
+  float s = __fdiv_rn(fmax, amax);
+  if (__float_as_uint(s) == 0x7F800000u) s = __uint_as_float(0x7F7FFFFFu);
+  return s * __builtin_ldexpf(1.0f, -margin);
+}
+
+// 2^-e as binary32 for e in [-127, 127] (2^-127 is the subnormal 0x00400000).
+__device__ __forceinline__ float pow2_neg(int e) {
+  return e == 127 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)(127 - e) << 23);
+}
+
+// MXFP8 shared exponent of a block from its amax bit pattern (non-negative,
+// NaN canonicalised): amax = 2^E (1 + f).  CEIL: E - emax + [f > 0.75];
+// OCP floor: E - emax.  Then + margin, clamp to [-127, 127]; amax 0 -> 0.
+__device__ __forceinline__ int mx_exponent(uint32_t abits, int emax_elem, bool ceil_rule, int margin) {
+  if (abits == 0u) return 0;
+  uint32_t ef = abits >> 23;
+  uint32_t man = abits & 0x7FFFFFu;
+  int E;
+  uint32_t fbits;
+  if (ef == 0u) {
+    int p = 31 - __clz(man);  // leading one of the subnormal significand
+    E = p - 149;
+    fbits = (man << (23 - p)) & 0x7FFFFFu;
+  } else {
+    E = (int)ef - 127;
+    fbits = man;
+  }
+  int e = E - emax_elem + ((ceil_rule && fbits > 0x600000u) ? 1 : 0) + margin;
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  return e;
+}
+
+}  // namespace qsg

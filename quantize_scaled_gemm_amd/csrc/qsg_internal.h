@@ -1,0 +1,27 @@
+// Internal launchers behind the C ABI.  Arguments have been validated by the
+// caller (qsg_api.hip); every launcher only enqueues work on `st`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsg {
+
+void launch_fill_u32(uint32_t* p, uint32_t v, int n, hipStream_t st);
+void launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, float* amax,
+                 hipStream_t st);
+void launch_compute_scale(const float* amax, int fmt, int margin, float* scale, float* scale_inv,
+                          hipStream_t st);
+void launch_amax_update(float* history, int64_t L, int64_t step, const float* amax, int fmt,
+                        int margin, float* scale, float* scale_inv, hipStream_t st);
+void launch_cast_transpose(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                           int fmt, const float* scale, uint8_t* q, uint8_t* qt, float* amax_out,
+                           hipStream_t st);
+void launch_quantize_blocked(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                             int scaling, int fmt, int margin, bool mx_ceil, uint8_t* q, void* s,
+                             uint8_t* qt, void* st_, hipStream_t st);
+void launch_scaled_gemm(const uint8_t* a, int fa, int ka, const void* sa, const uint8_t* b, int fb,
+                        int kb, const void* sb, int64_t M, int64_t N, int64_t K, int64_t lda,
+                        int64_t ldb, void* c, int c_dtype, int64_t ldc, hipStream_t st);
+
+}  // namespace qsg

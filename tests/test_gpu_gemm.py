@@ -1,0 +1,203 @@
+"""GPU parity of the scaled FP8 GEMM against the fp64 oracle.
+
+The GEMM consumes the same FP8 bytes and scales on both sides.  Integer-valued
+operands make the result exact in binary32, so those outputs must be
+bit-exact (fp32 out) or equal to the correctly rounded bf16 of the exact
+integer (bf16 out).  Everything else must pass the acceptance rule
+|y - ref| <= 1e-2 |ref| + 1e-3 rms(ref).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from helpers import f32_to_bf16_rne_f64, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+FMT_NAMES = {0: "e4m3", 1: "e5m2"}
+
+
+@pytest.fixture(scope="module")
+def q():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import quantize_scaled_gemm_amd as q
+
+    q.load_library()
+    return q
+
+
+def rand_codes(g, shape, fmt, lim=None):
+    """Random finite FP8 codes (optionally only values with |v| <= lim)."""
+    t = oracle.decode_table(fmt)
+    ok = np.isfinite(t)
+    if lim is not None:
+        ok &= np.abs(np.nan_to_num(t)) <= lim
+    finite = np.nonzero(ok)[0]
+    return finite[g.integers(0, finite.size, size=shape)].astype(np.uint8)
+
+
+def gemm(q, qa, fa, ka, sa, qb, fb, kb, sb, out="bf16"):
+    import torch
+
+    M, N = qa.shape[0], qb.shape[0]
+    c = torch.full((M, N), float("nan"), device="cuda",
+                   dtype=torch.bfloat16 if out == "bf16" else torch.float32)
+    q.qsg_scaled_gemm(qa, fa, ka, sa, qb, fb, kb, sb, c)
+    return to_np(c).astype(np.float64)
+
+
+def dscal(v):
+    import torch
+
+    return torch.tensor([v], dtype=torch.float32, device="cuda")
+
+
+SHAPES = [(128, 128, 128), (256, 384, 512), (130, 250, 300), (1, 1, 1), (37, 300, 1000),
+          (512, 256, 4096), (300, 200, 64), (64, 64, 16)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_integer_exact(q, M, N, K):
+    g = workloads.generator(40, M, N, K)
+    ia = g.integers(-15, 16, (M, K))
+    ib = g.integers(-15, 16, (N, K))
+    qa = oracle.encode(ia.astype(np.float32), "e4m3")
+    qb = oracle.encode(ib.astype(np.float32), "e4m3")
+    exact = (ia @ ib.T).astype(np.float64)  # |exact| < 2^24: exact in binary32
+    y32 = gemm(q, to_dev(qa), 0, 0, dscal(1.0), to_dev(qb), 0, 0, dscal(1.0), out="f32")
+    assert np.array_equal(y32, exact)
+    y16 = gemm(q, to_dev(qa), 0, 0, dscal(1.0), to_dev(qb), 0, 0, dscal(1.0), out="bf16")
+    assert np.array_equal(y16, f32_to_bf16_rne_f64(exact))
+
+
+@pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0), (0, 1), (1, 1)])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (130, 250, 300), (77, 129, 1024)])
+def test_per_tensor_random(q, fa, fb, M, N, K):
+    g = workloads.generator(41, fa, fb, M, N, K)
+    qa = rand_codes(g, (M, K), FMT_NAMES[fa], lim=400)
+    qb = rand_codes(g, (N, K), FMT_NAMES[fb], lim=400)
+    sa, sb = np.float32(0.0123), np.float32(7.5)
+    ref = oracle.gemm_per_tensor(qa, FMT_NAMES[fa], sa, qb, FMT_NAMES[fb], sb)
+    for out in ("bf16", "f32"):
+        y = gemm(q, to_dev(qa), fa, 0, dscal(sa), to_dev(qb), fb, 0, dscal(sb), out=out)
+        ok, info = oracle.tolerance_check(y, ref)
+        assert ok, info
+
+
+def test_strided_operands_and_output(q):
+    import torch
+
+    g = workloads.generator(42)
+    M, N, K = 192, 160, 512
+    qa_big = rand_codes(g, (M, K + 64), "e4m3", lim=100)
+    qb_big = rand_codes(g, (N, K + 32), "e4m3", lim=100)
+    qa, qb = qa_big[:, 16:16 + K], qb_big[:, :K]
+    ref = oracle.gemm_per_tensor(qa, "e4m3", 1.0, qb, "e4m3", 1.0)
+    cbig = torch.zeros((M, N + 8), device="cuda", dtype=torch.float32)
+    c = cbig[:, 4:4 + N]
+    q.qsg_scaled_gemm(to_dev(qa_big)[:, 16:16 + K], 0, 0, dscal(1.0), to_dev(qb_big)[:, :K], 0, 0,
+                      dscal(1.0), c)
+    assert oracle.tolerance_check(to_np(c), ref)[0]
+    assert np.all(to_np(cbig)[:, :4] == 0) and np.all(to_np(cbig)[:, 4 + N:] == 0)
+    # K not a multiple of 16 and an odd lda: element-wise loads
+    qa2 = rand_codes(g, (M, 77), "e4m3", lim=100)
+    qb2 = rand_codes(g, (N, 77), "e5m2", lim=100)
+    ref2 = oracle.gemm_per_tensor(qa2, "e4m3", 2.0, qb2, "e5m2", 0.5)
+    y = gemm(q, to_dev(qa2), 0, 0, dscal(2.0), to_dev(qb2), 1, 0, dscal(0.5), out="f32")
+    assert oracle.tolerance_check(y, ref2)[0]
+
+
+def test_k_zero_gives_zeros(q):
+    import torch
+
+    a = torch.empty((64, 0), dtype=torch.uint8, device="cuda")
+    b = torch.empty((32, 0), dtype=torch.uint8, device="cuda")
+    c = torch.full((64, 32), 5.0, device="cuda")
+    q.qsg_scaled_gemm(a, 0, 0, dscal(1.0), b, 0, 0, dscal(1.0), c)
+    assert np.all(to_np(c) == 0)
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (256, 384, 512), (160, 96, 4096), (33, 65, 96)])
+def test_mx_gemm(q, M, N, K):
+    g = workloads.generator(43, M, N, K)
+    qa = rand_codes(g, (M, K), "e4m3")
+    qb = rand_codes(g, (N, K), "e4m3")
+    sa = g.integers(117, 137, (M, K // 32)).astype(np.uint8)
+    sb = g.integers(117, 137, (N, K // 32)).astype(np.uint8)
+    ref = oracle.gemm_mx(qa, "e4m3", sa, qb, "e4m3", sb)
+    for out in ("bf16", "f32"):
+        y = gemm(q, to_dev(qa), 0, q.MXFP8, to_dev(sa), to_dev(qb), 0, q.MXFP8, to_dev(sb), out=out)
+        ok, info = oracle.tolerance_check(y, ref)
+        assert ok, info
+
+
+def test_mx_gemm_power_of_two_exact(q):
+    # integer codes with E8M0 scales: every partial sum is exact in binary32
+    g = workloads.generator(44)
+    M, N, K = 96, 64, 256
+    ia = g.integers(-8, 9, (M, K))
+    ib = g.integers(-8, 9, (N, K))
+    sa = g.integers(125, 130, (M, K // 32)).astype(np.uint8)
+    sb = g.integers(125, 130, (N, K // 32)).astype(np.uint8)
+    qa = oracle.encode(ia.astype(np.float32), "e4m3")
+    qb = oracle.encode(ib.astype(np.float32), "e4m3")
+    ref = oracle.gemm_mx(qa, "e4m3", sa, qb, "e4m3", sb)
+    y = gemm(q, to_dev(qa), 0, q.MXFP8, to_dev(sa), to_dev(qb), 0, q.MXFP8, to_dev(sb), out="f32")
+    assert np.array_equal(y, ref)
+
+
+@pytest.mark.parametrize("layout", ["128x128", "1x128"])
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (256, 384, 512), (200, 130, 1024)])
+def test_block_gemm(q, layout, M, N, K):
+    g = workloads.generator(45, M, N, K, 0 if layout == "128x128" else 1)
+    qa = rand_codes(g, (M, K), "e4m3")
+    qb = rand_codes(g, (N, K), "e4m3")
+    sa = g.uniform(1e-3, 1e-1, (M, K // 128)).astype(np.float32)
+    if layout == "128x128":
+        sb = g.uniform(1e-3, 1e-1, ((N + 127) // 128, K // 128)).astype(np.float32)
+        kb = 4
+    else:
+        sb = g.uniform(1e-3, 1e-1, (N, K // 128)).astype(np.float32)
+        kb = 3
+    ref = oracle.gemm_block(qa, "e4m3", sa, qb, "e4m3", sb, layout)
+    y = gemm(q, to_dev(qa), 0, 3, to_dev(sa), to_dev(qb), 0, kb, to_dev(sb), out="bf16")
+    ok, info = oracle.tolerance_check(y, ref)
+    assert ok, info
+
+
+def test_linear_fwd_bwd_tensorwise_hybrid(q):
+    """A small Linear: quantize X, W (E4M3) and dY (E5M2) with the library,
+    then fprop / dgrad / wgrad through the transposed copies; every byte and
+    scale bit-exact, every GEMM within the acceptance rule."""
+    import torch
+
+    M, K, N = 512, 384, 256
+    x = workloads.normal([46, 0], (M, K), 1.0)
+    w = workloads.normal([46, 1], (N, K), 0.02)
+    dy = workloads.normal([46, 2], (M, N), 1e-3)
+    from helpers import bf16_bits_to_f32, to_dev_bf16
+
+    res = {}
+    for name, bits, fmt, code in (("x", x, "e4m3", 0), ("w", w, "e4m3", 0), ("dy", dy, "e5m2", 1)):
+        R, C = bits.shape
+        qq = torch.empty((R, C), dtype=torch.uint8, device="cuda")
+        qt = torch.empty((C, R), dtype=torch.uint8, device="cuda")
+        s = torch.zeros(3, device="cuda")
+        q.qsg_quantize(to_dev_bf16(bits), q.TENSORWISE, code, q=qq, s=s, qt=qt)
+        rq, rqt, _, _, rsi = oracle.quantize_tensorwise(bf16_bits_to_f32(bits), fmt)
+        assert np.array_equal(to_np(qq), rq) and np.array_equal(to_np(qt), rqt)
+        assert to_np(s)[2] == rsi
+        res[name] = (qq, qt, s[2:3], rq, rqt, rsi)
+    qx, qxt, sx, rqx, rqxt, rsx = res["x"]
+    qw, qwt, sw, rqw, rqwt, rsw = res["w"]
+    qd, qdt, sd, rqd, rqdt, rsd = res["dy"]
+    y = gemm(q, qx, 0, 0, sx, qw, 0, 0, sw)
+    assert oracle.tolerance_check(y, oracle.gemm_per_tensor(rqx, "e4m3", rsx, rqw, "e4m3", rsw))[0]
+    dx = gemm(q, qd, 1, 0, sd, qwt, 0, 0, sw)
+    assert oracle.tolerance_check(dx, oracle.gemm_per_tensor(rqd, "e5m2", rsd, rqwt, "e4m3", rsw))[0]
+    dw = gemm(q, qdt, 1, 0, sd, qxt, 0, 0, sx)
+    assert oracle.tolerance_check(dw, oracle.gemm_per_tensor(rqdt, "e5m2", rsd, rqxt, "e4m3", rsx))[0]

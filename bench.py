@@ -1,0 +1,288 @@
+"""Benchmark: one FP8 Linear fwd+bwd step on one MI355X.
+
+Workload (the 4096-hidden Linear, tensorwise current scaling, hybrid
+formats): X[32768 x 4096] bf16 feeds two Linears, W[4096 x 4096] and
+W2[14336 x 4096]; their output gradients are dY[32768 x 4096] and
+dY2[32768 x 14336].  One step is the whole hot path:
+
+  for X, W, W2 (E4M3) and dY, dY2 (E5M2):  amax -> scale -> cast + transpose
+  fprop  Y = X W^T,  Y2 = X W2^T                 (E4M3 x E4M3)
+  dgrad  dX = dY W,  dX2 = dY2 W2                (E5M2 x E4M3)
+  wgrad  dW = dY^T X, dW2 = dY2^T X              (E5M2 x E4M3)
+
+All outputs bf16.  Inputs are seeded synthetic tensors (workloads.py), resident
+in HBM before timing starts.  `value` is whole-step throughput: the step's
+14.84 TFLOP of GEMM work divided by the step time (quantization included).
+Per-kernel times come from HIP events on the launch stream.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Prints one JSON line on stdout.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 scaled-GEMM TFLOPS + cast-transpose GB/s (%peak), 4096-hidden Linear"
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+M, H, F = 32768, 4096, 14336
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "quantize_scaled_gemm_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def gemm_flops(m, n, k):
+    return 2.0 * m * n * k
+
+
+class Timer:
+    """HIP events recorded on the launch stream, grouped by kernel name."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.marks = []  # (name, start_event, end_event, work, work_unit)
+
+    def run(self, name, work, fn):
+        ev0 = self.torch.cuda.Event(enable_timing=True)
+        ev1 = self.torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        fn()
+        ev1.record()
+        self.marks.append((name, ev0, ev1, work))
+
+    def summary(self):
+        out = {}
+        for name, e0, e1, work in self.marks:
+            ms = e0.elapsed_time(e1)
+            d = out.setdefault(name, {"launches": 0, "ms": 0.0, "work": 0.0})
+            d["launches"] += 1
+            d["ms"] += ms
+            d["work"] += work
+        return out
+
+
+def build_step(torch, q, dev):
+    import numpy as np
+
+    import workloads
+
+    t0 = time.time()
+    host = workloads.linear_4096(M, H, F)
+    log(f"[bench] generated inputs in {time.time() - t0:.1f}s")
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    X, W, W2, dY, dY2 = (to_dev(host[k]) for k in ("X", "W", "W2", "dY", "dY2"))
+    del host
+    u8 = dict(dtype=torch.uint8, device=dev)
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    tens = {}
+    for name, x, fmt in (("X", X, q.E4M3), ("W", W, q.E4M3), ("W2", W2, q.E4M3),
+                         ("dY", dY, q.E5M2), ("dY2", dY2, q.E5M2)):
+        r, c = x.shape
+        tens[name] = dict(x=x, fmt=fmt, q=torch.empty((r, c), **u8), qt=torch.empty((c, r), **u8),
+                          amax=torch.zeros(1, device=dev), scale=torch.zeros(1, device=dev),
+                          sinv=torch.zeros(1, device=dev))
+    outs = dict(Y=torch.empty((M, H), **bf), Y2=torch.empty((M, F), **bf),
+                dX=torch.empty((M, H), **bf), dX2=torch.empty((M, H), **bf),
+                dW=torch.empty((H, H), **bf), dW2=torch.empty((F, H), **bf))
+
+    T = q.TENSORWISE
+
+    def quantize(timer, name):
+        t = tens[name]
+        r, c = t["x"].shape
+        timer.run("amax", 2.0 * r * c, lambda: q.qsg_amax(t["x"], t["amax"]))
+        timer.run("compute_scale", 0.0,
+                  lambda: q.qsg_compute_scale(t["amax"], t["fmt"], 0, t["scale"], t["sinv"]))
+        timer.run("cast_transpose", 4.0 * r * c,
+                  lambda: q.qsg_cast_transpose(t["x"], t["fmt"], t["scale"], t["q"], t["qt"]))
+
+    def gemm(timer, kname, a, fa, sa, b, fb, sb, c):
+        m, k = a.shape
+        n = b.shape[0]
+        timer.run(kname, gemm_flops(m, n, k),
+                  lambda: q.qsg_scaled_gemm(a, fa, T, sa, b, fb, T, sb, c))
+
+    def step(timer):
+        for n in ("X", "W", "W2"):
+            quantize(timer, n)
+        x, w, w2 = tens["X"], tens["W"], tens["W2"]
+        gemm(timer, "gemm_e4m3_e4m3", x["q"], q.E4M3, x["sinv"], w["q"], q.E4M3, w["sinv"], outs["Y"])
+        gemm(timer, "gemm_e4m3_e4m3", x["q"], q.E4M3, x["sinv"], w2["q"], q.E4M3, w2["sinv"], outs["Y2"])
+        for n in ("dY", "dY2"):
+            quantize(timer, n)
+        d, d2 = tens["dY"], tens["dY2"]
+        gemm(timer, "gemm_e5m2_e4m3", d["q"], q.E5M2, d["sinv"], w["qt"], q.E4M3, w["sinv"], outs["dX"])
+        gemm(timer, "gemm_e5m2_e4m3", d2["q"], q.E5M2, d2["sinv"], w2["qt"], q.E4M3, w2["sinv"], outs["dX2"])
+        gemm(timer, "gemm_e5m2_e4m3", d["qt"], q.E5M2, d["sinv"], x["qt"], q.E4M3, x["sinv"], outs["dW"])
+        gemm(timer, "gemm_e5m2_e4m3", d2["qt"], q.E5M2, d2["sinv"], x["qt"], q.E4M3, x["sinv"], outs["dW2"])
+
+    step_flops = 3 * (gemm_flops(M, H, H) + gemm_flops(M, F, H))
+    step_elems = M * H + H * H + F * H + M * H + M * F
+    return step, step_flops, step_elems
+
+
+def cpu_baseline(step_flops, step_elems):
+    """The oracle, untuned, on a bounded sample of the same workload, scaled
+    to the step's TFLOP/s."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - informational only
+        blas_threads = 1
+
+    # quantization sample: amax + scale + cast + transpose of 4096 rows of X
+    rows_q = 4096
+    xs = workloads.bf16_bits_to_f32(workloads.linear_4096(rows_q, H, F, which=("X",))["X"])
+    t0 = time.perf_counter()
+    oracle.quantize_tensorwise(xs, "e4m3")
+    tq = time.perf_counter() - t0
+    per_elem = tq / xs.size
+
+    # GEMM sample: fp64 product of the dequantized operands, 2048 rows of X
+    # against 4096 rows of W2 (a slab of the fprop of the larger Linear)
+    rows_g = 2048
+    w2 = workloads.bf16_bits_to_f32(workloads.linear_4096(M, H, F, which=("W2",))["W2"][:H])
+    qx, _, _, _, sxi = oracle.quantize_tensorwise(xs[:rows_g], "e4m3")
+    qw, _, _, _, swi = oracle.quantize_tensorwise(w2, "e4m3")
+    t0 = time.perf_counter()
+    oracle.gemm_per_tensor(qx, "e4m3", sxi, qw, "e4m3", swi)
+    tg = time.perf_counter() - t0
+    gemm_rate = gemm_flops(rows_g, H, H) / tg
+
+    step_time = per_elem * step_elems + step_flops / gemm_rate
+    return {
+        "value": step_flops / step_time / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": (f"tensorwise quantize of {rows_q}x{H} rows of X ({tq:.2f}s, numpy, 1 thread) and the "
+                   f"fp64 fprop GEMM of {rows_g} rows of X against the first {H} rows of W2 ({tg:.2f}s, BLAS "
+                   f"{blas_threads} threads), extrapolated to the full step's {step_elems/1e6:.0f}M quantized "
+                   f"elements and {step_flops/1e12:.2f} TFLOP"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        log(f"bench.py measures one GPU only: the FP8 Linear hot path here is the single-GPU "
+            f"kernel work; --gpus {args.gpus} is not supported (run with --gpus 1).")
+        sys.exit(2)
+
+    import torch
+
+    import quantize_scaled_gemm_amd as q
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q.load_library()
+
+    step, step_flops, step_elems = build_step(torch, q, dev)
+
+    for _ in range(args.warmup):
+        step(Timer(torch))
+    torch.cuda.synchronize()
+
+    timer = Timer(torch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(timer)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    ks = timer.summary()
+    kernels = {}
+    for name, d in ks.items():
+        avg_ms = d["ms"] / d["launches"]
+        rec = {"launches_per_step": d["launches"] // args.steps, "avg_ms": round(avg_ms, 4)}
+        if name.startswith("gemm"):
+            tf = d["work"] / (d["ms"] * 1e-3) / 1e12
+            rec.update({"TFLOP/s": round(tf, 1), "frac": round(tf / PEAK_FP8_TFLOPS, 4)})
+        elif d["work"] > 0:
+            gb = d["work"] / (d["ms"] * 1e-3) / 1e9
+            rec.update({"GB/s": round(gb, 1), "frac": round(gb / PEAK_HBM_GBPS, 4)})
+        kernels[name] = rec
+
+    gemm_ms = sum(d["ms"] for n, d in ks.items() if n.startswith("gemm")) / args.steps
+    dom = max((n for n in ks if n.startswith("gemm")), key=lambda n: ks[n]["ms"])
+    dd = ks[dom]
+    achieved = dd["work"] / (dd["ms"] * 1e-3) / 1e12
+    ct = ks["cast_transpose"]
+    ct_gbps = ct["work"] / (ct["ms"] * 1e-3) / 1e9
+
+    traffic = None
+    prof_path = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(prof_path):
+        with open(prof_path) as fh:
+            tr = json.load(fh).get(dom)
+        if tr and tr.get("source_hash") == source_hash("gemm.hip"):
+            traffic = tr.get("bytes_per_launch")
+
+    line = {
+        "metric": METRIC,
+        "value": round(step_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": "linear_4096: tensorwise hybrid FP8 Linear fwd+bwd, X 32768x4096, "
+                               "W 4096x4096, W2 14336x4096, bf16 in/out",
+                   "tokens": M, "hidden": H, "ffn": F, "recipe": "tensorwise",
+                   "formats": "E4M3 X/W, E5M2 dY"},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic},
+        "gemm_tflops": round(step_flops / (gemm_ms * 1e-3) / 1e12, 1),
+        "cast_transpose_gbps": round(ct_gbps, 1),
+        "cast_transpose_frac": round(ct_gbps / PEAK_HBM_GBPS, 4),
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        line["cpu_baseline"] = cpu_baseline(step_flops, step_elems)
+        log(f"[bench] cpu baseline took {time.time() - t0:.1f}s")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

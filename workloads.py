@@ -4,11 +4,14 @@ This module only draws random tensors; it holds none of the quantization or
 GEMM arithmetic.  Both the GPU tests / bench and the CPU oracle take their
 inputs from here.
 
-Recipe (for every tensor): a numpy ``Generator(PCG64(SeedSequence(key)))``
-draws fp64 samples in row chunks of ``CHUNK_ROWS`` rows, sequentially from one
-generator; the samples are multiplied by the tensor's standard deviation,
-rounded to binary32 (numpy, round-to-nearest-even) and, for bfloat16 tensors,
-rounded again to bfloat16 by round-to-nearest-even on the bit pattern.
+Recipe (for every tensor): the tensor is cut into row chunks of
+``CHUNK_ROWS`` rows; chunk c is drawn by its own numpy
+``Generator(PCG64(SeedSequence(key + [c])))`` (so chunks can be drawn in
+parallel threads); normal samples are drawn in binary32
+(``standard_normal(dtype=float32)``), Student-t samples in fp64 and rounded to
+binary32; the samples are multiplied by the tensor's standard deviation in
+binary32 and, for bfloat16 tensors, rounded to bfloat16 by
+round-to-nearest-even on the bit pattern.
 bfloat16 tensors are returned as their uint16 bit patterns; fp32 tensors as
 float32 arrays.  ``key`` is ``[workload, tensor index]`` (plus the step for
 per-step tensors).
@@ -25,9 +28,13 @@ Workloads (shapes and distributions of the FP8 Linear configurations):
                    ~N(0,0.02); dY 32768x4096 and dY2 32768x14336 ~N(0,1e-3)
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 CHUNK_ROWS = 1024
+_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 WORKLOAD_IDS = {
     "tensorwise_256": 1,
@@ -57,20 +64,26 @@ def bf16_bits_to_f32(b):
 
 def _draw(key, shape, draw_fn, std, dtype):
     rows, cols = shape
-    g = generator(*key)
-    if dtype == "bf16":
-        out = np.empty((rows, cols), dtype=np.uint16)
-    else:
-        out = np.empty((rows, cols), dtype=np.float32)
-    for r0 in range(0, rows, CHUNK_ROWS):
+    out = np.empty((rows, cols), dtype=np.uint16 if dtype == "bf16" else np.float32)
+
+    def chunk(c):
+        r0 = c * CHUNK_ROWS
         r1 = min(rows, r0 + CHUNK_ROWS)
-        v = (draw_fn(g, (r1 - r0, cols)) * std).astype(np.float32)
+        v = draw_fn(generator(*key, c), (r1 - r0, cols)).astype(np.float32) * np.float32(std)
         out[r0:r1] = f32_to_bf16_bits(v) if dtype == "bf16" else v
+
+    n = (rows + CHUNK_ROWS - 1) // CHUNK_ROWS
+    if n <= 1:
+        for c in range(n):
+            chunk(c)
+    else:
+        with ThreadPoolExecutor(max_workers=min(n, _THREADS)) as ex:
+            list(ex.map(chunk, range(n)))
     return out
 
 
 def normal(key, shape, std=1.0, dtype="bf16"):
-    return _draw(key, shape, lambda g, s: g.standard_normal(s), std, dtype)
+    return _draw(key, shape, lambda g, s: g.standard_normal(s, dtype=np.float32), std, dtype)
 
 
 def student_t(key, shape, nu=3.0, dtype="bf16"):

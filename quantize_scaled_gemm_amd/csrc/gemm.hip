@@ -339,6 +339,10 @@ void launch_fmt(const GemmArgs& g, int fa, int fb, bool out_bf16, hipStream_t st
 void launch_scaled_gemm(const uint8_t* a, int fa, int ka, const void* sa, const uint8_t* b, int fb,
                         int kb, const void* sb, int64_t M, int64_t N, int64_t K, int64_t lda,
                         int64_t ldb, void* c, int c_dtype, int64_t ldc, hipStream_t st) {
+  const bool per_tensor = (ka == 0 || ka == 1) && (kb == 0 || kb == 1);
+  if ((per_tensor || ka == 2) &&
+      launch_scaled_gemm_fast(a, fa, ka == 2, sa, b, fb, sb, M, N, K, lda, ldb, c, c_dtype, ldc, st))
+    return;
   constexpr int BM = 128, BN = 128;
   GemmArgs g{};
   g.a = a; g.b = b; g.sa = sa; g.sb = sb;

@@ -1,0 +1,351 @@
+// Large-tile scaled FP8 GEMM for gfx950 (per-tensor and MXFP8 scales):
+//   C[m,n] = sum_k (A[m,k] sa) (B[n,k] sb),  A M x K, B N x K, K-contiguous.
+// ("Low-Precision Training Guide", section "When to Use Low Precision": the
+// FP8 GEMMs of a Linear; recipe "mxfp8": E8M0 scale per 1 x 32 block.)
+//
+// Design for MI355X.
+//   * 256 x 256 x 128 workgroup tile, 256 threads = 4 wave64s in 2 x 2, each
+//     wave 128 x 128 = 4 x 4 MFMA tiles of v_mfma(_scale)_f32_32x32x64_f8f6f4
+//     (256 fp32 accumulators per lane).  At this tile size a workgroup needs
+//     64 KB of operand data per 128-K step for 2048 MFMA cycles per SIMD, i.e.
+//     32 B/clk/CU from L2, half of what a 128 x 128 tile needs.
+//   * Operands go global -> LDS directly (global_load_lds_dwordx4), without
+//     passing through VGPRs.  Such a load writes lane L's 16 bytes to LDS slot
+//     L of a 1 KB block, so the swizzled LDS layout (16-byte chunk c of row r
+//     at position c ^ (r & 7) of the row, which makes the 16-byte fragment
+//     reads of 8 consecutive rows conflict-free) is produced by choosing, per
+//     lane, which (row, chunk) of global memory it fetches.  Rows past M / N
+//     are clamped to the last row (their results are never stored).
+//   * Two LDS stages (2 x 64 KB): the loads of K tile t+1 are in flight while
+//     tile t is multiplied; one barrier per K tile.
+//   * MXFP8: the 4 E8M0 bytes of a row for the tile's 4 K blocks travel with
+//     the tile (global_load_lds_dword); lane half h shifts its row's word by
+//     8h so that op_sel 0 / 2 pick the bytes of K blocks h / 2+h for the two
+//     64-K MFMA steps (the MFMA operand K order: lane half h holds K
+//     [16h, 16h+16) and [32+16h, 48+16h) of a step; the scale of lanes 0..31
+//     covers K 0..31 and that of lanes 32..63 covers K 32..63).
+//   * Tile order: workgroup ids are dispatched round-robin over the 8 XCDs;
+//     they are remapped so each XCD owns a contiguous range of tiles, walked
+//     in groups of 4 tile-rows x all tile-columns, so the 32 tiles an XCD runs
+//     at once share 4 A panels and 8 B panels in its L2.
+#include <hip/hip_runtime.h>
+
+#include "qsg_device.h"
+#include "qsg_internal.h"
+
+namespace qsg {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+constexpr int FBM = 256, FBN = 256, FBK = 128;
+constexpr int CH = FBK / 16;  // 16-byte chunks per LDS row
+
+struct FastArgs {
+  const uint8_t* a;
+  const uint8_t* b;
+  const void* sa;
+  const void* sb;
+  int64_t M, N, K, lda, ldb, ldc;
+  void* c;
+  bool vec_c;
+  int64_t tiles_m, tiles_n;
+};
+
+// Byte offsets (from the operand base, without k0) of the chunks this thread
+// fetches for a ROWS-row tile: instruction i of wave w fills 1 KB block
+// i * 4 + w of the stage.
+template <int ROWS>
+__device__ __forceinline__ void chunk_offsets(uint32_t (&off)[ROWS * CH / 256], int64_t row0, int64_t nrows,
+                                              int64_t ld) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < ROWS * CH / 256; ++i) {
+    const int blk = i * 4 + wave;
+    const int slot = blk * 64 + lane;
+    const int row = slot / CH, pc = slot % CH;
+    const int c = pc ^ (row & 7);
+    int64_t gr = row0 + row;
+    if (gr > nrows - 1) gr = nrows - 1;
+    off[i] = (uint32_t)(gr * ld + c * 16);
+  }
+}
+
+template <int ROWS>
+__device__ __forceinline__ void issue_tile(const uint8_t* base, const uint32_t (&off)[ROWS * CH / 256],
+                                           int64_t k0, uint8_t* lds) {
+  const int wave = threadIdx.x >> 6;
+  const uint8_t* p = base + k0;
+#pragma unroll
+  for (int i = 0; i < ROWS * CH / 256; ++i) {
+    const int blk = i * 4 + wave;
+    __builtin_amdgcn_global_load_lds((const void*)(p + off[i]), (lds_ptr_t)(lds + blk * 1024), 16, 0, 0);
+  }
+}
+
+// A 32-row fragment: `row_off` is the byte offset of this lane's row of the
+// first 32-row slice, `c_lo` / `c_hi` the swizzled byte offsets of its two
+// 16-byte chunks (the swizzle only depends on row & 7, which is the same for
+// every 32-row slice), and slice i adds i * 32 rows as an immediate.
+__device__ __forceinline__ v8i ffrag(const uint8_t* lds, int row_off, int slice, int c_lo, int c_hi) {
+  const uint8_t* p = lds + row_off + slice * 32 * FBK;
+  uint4 lo = *reinterpret_cast<const uint4*>(p + c_lo);
+  uint4 hi = *reinterpret_cast<const uint4*>(p + c_hi);
+  v8i r;
+  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+  return r;
+}
+
+constexpr int TMW = FBM / 2 / 32, TNW = FBN / 2 / 32;  // MFMA tiles per wave
+
+struct Frags {
+  v8i a[TMW], b[TNW];
+  int sa[TMW], sb[TNW];  // MX: E8M0 words (byte 0: first 64-K step, byte 2: second)
+};
+
+// The operand tiles of the two LDS stages are distinct __shared__ objects so
+// that the compiler can tell reads of one stage from the in-flight
+// global->LDS loads into the other (it then needs no vmcnt wait before them).
+__shared__ __attribute__((aligned(1024))) uint8_t lds_a0[FBM * FBK];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_a1[FBM * FBK];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_b0[FBN * FBK];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_b1[FBN * FBK];
+__shared__ __attribute__((aligned(256))) uint32_t lds_sa0[FBM];
+__shared__ __attribute__((aligned(256))) uint32_t lds_sa1[FBM];
+__shared__ __attribute__((aligned(256))) uint32_t lds_sb0[FBN];
+__shared__ __attribute__((aligned(256))) uint32_t lds_sb1[FBN];
+
+template <int S>
+__device__ __forceinline__ uint8_t* stage_a() { return S ? lds_a1 : lds_a0; }
+template <int S>
+__device__ __forceinline__ uint8_t* stage_b() { return S ? lds_b1 : lds_b0; }
+template <int S>
+__device__ __forceinline__ uint32_t* stage_sa() { return S ? lds_sa1 : lds_sa0; }
+template <int S>
+__device__ __forceinline__ uint32_t* stage_sb() { return S ? lds_sb1 : lds_sb0; }
+
+template <int S>
+__device__ __forceinline__ void issue_stage(const FastArgs& g, const uint32_t (&offa)[FBM * CH / 256],
+                                            const uint32_t (&offb)[FBN * CH / 256], const uint8_t* sa_row,
+                                            const uint8_t* sb_row, bool mx, int64_t kt) {
+  issue_tile<FBM>(g.a, offa, kt * FBK, stage_a<S>());
+  issue_tile<FBN>(g.b, offb, kt * FBK, stage_b<S>());
+  if (mx) {
+    const int wave = threadIdx.x >> 6;
+    __builtin_amdgcn_global_load_lds((const void*)(sa_row + kt * 4), (lds_ptr_t)(stage_sa<S>() + wave * 64), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(sb_row + kt * 4), (lds_ptr_t)(stage_sb<S>() + wave * 64), 4, 0, 0);
+  }
+}
+
+template <int S, bool MX>
+__device__ __forceinline__ void load_frags(Frags& f, int kk, int a_row_off, int b_row_off, int c_lo, int c_hi,
+                                           int a_srow, int b_srow, int sh) {
+#pragma unroll
+  for (int i = 0; i < TMW; ++i) f.a[i] = ffrag(stage_a<S>(), a_row_off, i, c_lo, c_hi);
+#pragma unroll
+  for (int j = 0; j < TNW; ++j) f.b[j] = ffrag(stage_b<S>(), b_row_off, j, c_lo, c_hi);
+  if constexpr (MX) {
+#pragma unroll
+    for (int i = 0; i < TMW; ++i) f.sa[i] = (int)(stage_sa<S>()[a_srow + i * 32] >> sh);
+#pragma unroll
+    for (int j = 0; j < TNW; ++j) f.sb[j] = (int)(stage_sb<S>()[b_srow + j * 32] >> sh);
+  }
+}
+
+template <bool MX, int FA, int FB>
+__device__ __forceinline__ void mfma_block(v16f (&acc)[TMW][TNW], const Frags& f) {
+#pragma unroll
+  for (int i = 0; i < TMW; ++i) {
+#pragma unroll
+    for (int j = 0; j < TNW; ++j) {
+      if constexpr (MX)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, 0, f.sb[j], 0, f.sa[i]);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, 0, 0, 0, 0);
+    }
+  }
+}
+
+template <bool MX, int FA, int FB, bool OUT_BF16>
+__global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
+  constexpr int WM = FBM / 2, WN = FBN / 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // tile coordinates: XCD-contiguous ranges, groups of 4 tile-rows
+  const int64_t T = g.tiles_m * g.tiles_n;
+  const int64_t bid = blockIdx.x;
+  const int64_t xcd = bid % 8, local = bid / 8;
+  const int64_t per = T / 8, rem = T % 8;
+  const int64_t logical = xcd * per + (xcd < rem ? xcd : rem) + local;
+  constexpr int64_t GM = 4;
+  const int64_t per_group = GM * g.tiles_n;
+  const int64_t first_m = (logical / per_group) * GM;
+  const int64_t gsize = (g.tiles_m - first_m) < GM ? (g.tiles_m - first_m) : GM;
+  const int64_t m0 = (first_m + (logical % per_group) % gsize) * FBM;
+  const int64_t n0 = ((logical % per_group) / gsize) * FBN;
+  const int64_t nk = g.K / FBK;  // even (checked by the launcher)
+
+  uint32_t offa[FBM * CH / 256], offb[FBN * CH / 256];
+  chunk_offsets<FBM>(offa, m0, g.M, g.lda);
+  chunk_offsets<FBN>(offb, n0, g.N, g.ldb);
+  const uint8_t* sa_row = nullptr;
+  const uint8_t* sb_row = nullptr;
+  if constexpr (MX) {
+    const int64_t nb = g.K / 32;
+    int64_t ra = m0 + threadIdx.x, rb = n0 + threadIdx.x;
+    if (ra > g.M - 1) ra = g.M - 1;
+    if (rb > g.N - 1) rb = g.N - 1;
+    sa_row = reinterpret_cast<const uint8_t*>(g.sa) + ra * nb;
+    sb_row = reinterpret_cast<const uint8_t*>(g.sb) + rb * nb;
+  }
+  // fragment addressing: lane half h reads chunks kk*4 + h and kk*4 + 2 + h
+  const int a_row_off = (wm * WM + (lane & 31)) * FBK;
+  const int b_row_off = (wn * WN + (lane & 31)) * FBK;
+  const int h = lane >> 5, x7 = lane & 7;
+  const int c00 = ((0 + h) ^ x7) << 4, c01 = ((2 + h) ^ x7) << 4;
+  const int c10 = ((4 + h) ^ x7) << 4, c11 = ((6 + h) ^ x7) << 4;
+  const int a_srow = wm * WM + (lane & 31), b_srow = wn * WN + (lane & 31);
+  // MX: bytes h (first 64-K step) and 2 + h (second) of the row's word
+  const int sh0 = 8 * h, sh1 = 8 * h + 16;
+
+  v16f acc[TMW][TNW];
+#pragma unroll
+  for (int i = 0; i < TMW; ++i)
+#pragma unroll
+    for (int j = 0; j < TNW; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  Frags f0, f1;
+  issue_stage<0>(g, offa, offb, sa_row, sb_row, MX, 0);
+  issue_stage<1>(g, offa, offb, sa_row, sb_row, MX, 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  load_frags<0, MX>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);
+
+  // One K tile in stage S (f0 holds its first 64-K fragments on entry): the
+  // second-step fragments are read while the first-step MFMAs run; after the
+  // barrier the tile two ahead is fetched into stage S and the next tile's
+  // first-step fragments are read from stage S^1 while the second-step MFMAs
+  // run.  Past the last tile the fetch repeats the last tile and the reads
+  // are unused, which keeps the body branch-free.
+#define QSG_FAST_STEP(S, KT)                                                                   \
+  {                                                                                            \
+    load_frags<S, MX>(f1, 1, a_row_off, b_row_off, c10, c11, a_srow, b_srow, sh1);             \
+    mfma_block<MX, FA, FB>(acc, f0);                                                           \
+    _Pragma("unroll") for (int q = 0; q < TMW * TNW; ++q) {                                    \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                       \
+    }                                                                                          \
+    __builtin_amdgcn_s_waitcnt(0);                                                             \
+    __syncthreads();                                                                           \
+    const int64_t nxt = (KT) + 2 < nk ? (KT) + 2 : nk - 1;                                     \
+    issue_stage<S>(g, offa, offb, sa_row, sb_row, MX, nxt);                                    \
+    load_frags<S ^ 1, MX>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);         \
+    mfma_block<MX, FA, FB>(acc, f1);                                                           \
+    _Pragma("unroll") for (int q = 0; q < TMW * TNW; ++q) {                                    \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);                                       \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);                                       \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);                                       \
+    }                                                                                          \
+  }
+
+  for (int64_t kt = 0; kt < nk; kt += 2) {
+    QSG_FAST_STEP(0, kt)
+    QSG_FAST_STEP(1, kt + 1)
+  }
+#undef QSG_FAST_STEP
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // ---- epilogue ------------------------------------------------------------
+  float alpha = 1.0f;
+  if constexpr (!MX) alpha = *reinterpret_cast<const float*>(g.sa) * *reinterpret_cast<const float*>(g.sb);
+#pragma unroll
+  for (int i = 0; i < TMW; ++i) {
+    const int64_t m = m0 + wm * WM + i * 32 + (lane & 31);
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int j = 0; j < TNW; ++j) {
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const int64_t n = n0 + wn * WN + j * 32 + grp * 8 + (lane >> 5) * 4;
+        const float v0 = acc[i][j][grp * 4 + 0] * alpha, v1 = acc[i][j][grp * 4 + 1] * alpha;
+        const float v2 = acc[i][j][grp * 4 + 2] * alpha, v3 = acc[i][j][grp * 4 + 3] * alpha;
+        if constexpr (OUT_BF16) {
+          uint16_t* c = reinterpret_cast<uint16_t*>(g.c) + m * g.ldc + n;
+          const uint16_t h0 = f32_to_bf16_rne(v0), h1 = f32_to_bf16_rne(v1);
+          const uint16_t h2 = f32_to_bf16_rne(v2), h3 = f32_to_bf16_rne(v3);
+          if (g.vec_c && n + 3 < g.N) {
+            *reinterpret_cast<uint2*>(c) = make_uint2((uint32_t)h0 | ((uint32_t)h1 << 16),
+                                                      (uint32_t)h2 | ((uint32_t)h3 << 16));
+          } else {
+            if (n + 0 < g.N) c[0] = h0;
+            if (n + 1 < g.N) c[1] = h1;
+            if (n + 2 < g.N) c[2] = h2;
+            if (n + 3 < g.N) c[3] = h3;
+          }
+        } else {
+          float* c = reinterpret_cast<float*>(g.c) + m * g.ldc + n;
+          if (g.vec_c && n + 3 < g.N) {
+            *reinterpret_cast<float4*>(c) = make_float4(v0, v1, v2, v3);
+          } else {
+            if (n + 0 < g.N) c[0] = v0;
+            if (n + 1 < g.N) c[1] = v1;
+            if (n + 2 < g.N) c[2] = v2;
+            if (n + 3 < g.N) c[3] = v3;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <bool MX, int FA, int FB>
+void launch_fast_cfg(const FastArgs& g, bool out_bf16, hipStream_t st) {
+  const unsigned grid = (unsigned)(g.tiles_m * g.tiles_n);
+  if (out_bf16)
+    hipLaunchKernelGGL((gemm_fast_kernel<MX, FA, FB, true>), dim3(grid), dim3(256), 0, st, g);
+  else
+    hipLaunchKernelGGL((gemm_fast_kernel<MX, FA, FB, false>), dim3(grid), dim3(256), 0, st, g);
+}
+
+template <bool MX>
+void launch_fast_fmt(const FastArgs& g, int fa, int fb, bool out_bf16, hipStream_t st) {
+  if (fa == kE4M3 && fb == kE4M3) launch_fast_cfg<MX, kE4M3, kE4M3>(g, out_bf16, st);
+  else if (fa == kE5M2 && fb == kE4M3) launch_fast_cfg<MX, kE5M2, kE4M3>(g, out_bf16, st);
+  else if (fa == kE4M3 && fb == kE5M2) launch_fast_cfg<MX, kE4M3, kE5M2>(g, out_bf16, st);
+  else launch_fast_cfg<MX, kE5M2, kE5M2>(g, out_bf16, st);
+}
+
+}  // namespace
+
+bool launch_scaled_gemm_fast(const uint8_t* a, int fa, bool mx, const void* sa, const uint8_t* b, int fb,
+                             const void* sb, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                             void* c, int c_dtype, int64_t ldc, hipStream_t st) {
+  // eligibility: whole 128-K tiles, 16-byte rows, 32-bit chunk offsets, enough tiles
+  if (K <= 0 || K % (2 * FBK) != 0) return false;
+  if ((uintptr_t)a % 16 || (uintptr_t)b % 16 || lda % 16 || ldb % 16) return false;
+  if (M * lda >= (int64_t)1 << 32 || N * ldb >= (int64_t)1 << 32) return false;
+  if (mx && ((uintptr_t)sa % 4 || (uintptr_t)sb % 4)) return false;
+  const int64_t tiles_m = (M + FBM - 1) / FBM, tiles_n = (N + FBN - 1) / FBN;
+  if (tiles_m * tiles_n < 128) return false;  // too few large tiles to fill the chip
+  FastArgs g{};
+  g.a = a; g.b = b; g.sa = sa; g.sb = sb;
+  g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.c = c;
+  const bool out_bf16 = (c_dtype == 1);
+  g.vec_c = out_bf16 ? (((uintptr_t)c % 8 == 0) && (ldc % 4 == 0)) : (((uintptr_t)c % 16 == 0) && (ldc % 4 == 0));
+  g.tiles_m = tiles_m;
+  g.tiles_n = tiles_n;
+  if (mx)
+    launch_fast_fmt<true>(g, fa, fb, out_bf16, st);
+  else
+    launch_fast_fmt<false>(g, fa, fb, out_bf16, st);
+  return true;
+}
+
+}  // namespace qsg

@@ -20,6 +20,12 @@ void launch_cast_transpose(const void* x, int dtype, int64_t rows, int64_t cols,
 void launch_quantize_blocked(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                              int scaling, int fmt, int margin, bool mx_ceil, uint8_t* q, void* s,
                              uint8_t* qt, void* st_, hipStream_t st);
+// 256x256x128 direct-to-LDS kernel for per-tensor (mx = false) and MXFP8
+// scales; returns false (and launches nothing) when the problem is not
+// eligible, in which case the general kernel is used.
+bool launch_scaled_gemm_fast(const uint8_t* a, int fa, bool mx, const void* sa, const uint8_t* b, int fb,
+                             const void* sb, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                             void* c, int c_dtype, int64_t ldc, hipStream_t st);
 void launch_scaled_gemm(const uint8_t* a, int fa, int ka, const void* sa, const uint8_t* b, int fb,
                         int kb, const void* sb, int64_t M, int64_t N, int64_t K, int64_t lda,
                         int64_t ldb, void* c, int c_dtype, int64_t ldc, hipStream_t st);

@@ -201,3 +201,69 @@ def test_linear_fwd_bwd_tensorwise_hybrid(q):
     assert oracle.tolerance_check(dx, oracle.gemm_per_tensor(rqd, "e5m2", rsd, rqwt, "e4m3", rsw))[0]
     dw = gemm(q, qdt, 1, 0, sd, qxt, 0, 0, sx)
     assert oracle.tolerance_check(dw, oracle.gemm_per_tensor(rqdt, "e5m2", rsd, rqxt, "e4m3", rsx))[0]
+
+
+# ---------------------------------------------------------------------------
+# the large-tile path (256 x 256 tiles; used when K % 256 == 0 and the
+# problem has at least 128 such tiles)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,K", [(2048, 4096, 256), (4096, 2048, 512)])
+def test_large_tile_integer_exact(q, M, N, K):
+    g = workloads.generator(47, M, N, K)
+    ia = g.integers(-15, 16, (M, K))
+    ib = g.integers(-15, 16, (N, K))
+    qa = oracle.encode(ia.astype(np.float32), "e4m3")
+    qb = oracle.encode(ib.astype(np.float32), "e4m3")
+    exact = (ia.astype(np.float64) @ ib.T.astype(np.float64))
+    y = gemm(q, to_dev(qa), 0, 0, dscal(1.0), to_dev(qb), 0, 0, dscal(1.0), out="f32")
+    assert np.array_equal(y, exact)
+    y16 = gemm(q, to_dev(qa), 0, 0, dscal(1.0), to_dev(qb), 0, 0, dscal(1.0), out="bf16")
+    assert np.array_equal(y16, f32_to_bf16_rne_f64(exact))
+
+
+@pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_large_tile_per_tensor(q, fa, fb):
+    M, N, K = 4096 + 100, 4096 - 36, 768  # ragged M and N: clamped rows, masked stores
+    g = workloads.generator(48, fa, fb)
+    qa = rand_codes(g, (M, K), FMT_NAMES[fa], lim=300)
+    qb = rand_codes(g, (N, K), FMT_NAMES[fb], lim=300)
+    sa, sb = np.float32(0.05), np.float32(3.0)
+    ref = oracle.gemm_per_tensor(qa, FMT_NAMES[fa], sa, qb, FMT_NAMES[fb], sb)
+    y = gemm(q, to_dev(qa), fa, 0, dscal(sa), to_dev(qb), fb, 0, dscal(sb), out="bf16")
+    ok, info = oracle.tolerance_check(y, ref)
+    assert ok, info
+
+
+def test_large_tile_mx(q):
+    """MX GEMM on what the quantizer produces: E4M3 codes and E8M0 scales of
+    seeded ~N(0, 0.02) data (ragged N)."""
+    M, N, K = 4096, 4096 + 64, 512
+    x = workloads.normal([49, 0], (M, K), 0.02, "f32")
+    w = workloads.normal([49, 1], (N, K), 0.02, "f32")
+    qx = oracle.mx_quantize(x, "e4m3", colwise=False)
+    qw = oracle.mx_quantize(w, "e4m3", colwise=False)
+    ref = oracle.gemm_mx(qx["q"], "e4m3", qx["s"], qw["q"], "e4m3", qw["s"])
+    y = gemm(q, to_dev(qx["q"]), 0, q.MXFP8, to_dev(qx["s"]), to_dev(qw["q"]), 0, q.MXFP8, to_dev(qw["s"]),
+             out="f32")
+    ok, info = oracle.tolerance_check(y, ref)
+    assert ok, info
+
+
+def test_mx_adversarial_scales_error_bound(q):
+    """Random codes over the whole E4M3 range with E8M0 block scales drawn over
+    20 binades: heavy cancellation.  The scaled MFMA accumulates such sums
+    less precisely than binary32; the measured error stays below
+    2^-10 * sum_k |a_k b_k| (2x above the worst case seen), which this test
+    asserts next to the 1e-2 relative term."""
+    M, N, K = 4096, 4096 + 64, 512
+    g = workloads.generator(49)
+    qa = rand_codes(g, (M, K), "e4m3")
+    qb = rand_codes(g, (N, K), "e4m3")
+    sa = g.integers(117, 137, (M, K // 32)).astype(np.uint8)
+    sb = g.integers(117, 137, (N, K // 32)).astype(np.uint8)
+    ref = oracle.gemm_mx(qa, "e4m3", sa, qb, "e4m3", sb)
+    absref = oracle.gemm_mx(qa & 0x7F, "e4m3", sa, qb & 0x7F, "e4m3", sb)
+    y = gemm(q, to_dev(qa), 0, q.MXFP8, to_dev(sa), to_dev(qb), 0, q.MXFP8, to_dev(sb), out="f32")
+    err = np.abs(y - ref)
+    assert np.all(err <= 1e-2 * np.abs(ref) + 2.0 ** -10 * absref)
+    assert np.linalg.norm(y - ref) / np.linalg.norm(ref) < 1e-3

@@ -193,6 +193,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB device-to-device copy three times (the reference "
+                         "kernel for scaling HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -210,6 +213,14 @@ def main():
     q.load_library()
 
     step, step_flops, step_elems = build_step(torch, q, dev)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step(Timer(torch))

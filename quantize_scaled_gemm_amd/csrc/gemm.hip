@@ -19,8 +19,8 @@
 //     four consecutive columns; the epilogue stores 8 bytes (4 bf16) per run.
 //   * Global -> LDS: each thread moves 16-byte chunks (8 lanes = one 128-byte
 //     K row of the tile); LDS rows are 128 bytes with the 16-byte chunk index
-//     XOR-swizzled by (row & 7), so the 16-byte fragment reads of 8
-//     consecutive rows hit all 32 banks.  Two LDS stages; the next K tile is
+//     XOR-swizzled by row (see swz), so the 16-byte fragment reads of 16
+//     consecutive rows hit all 64 banks.  Two LDS stages; the next K tile is
 //     fetched into registers while the current one is multiplied.
 //   * Scales: per-tensor scales multiply the fp32 accumulator in the epilogue;
 //     MXFP8 scales go to the MFMA; blockwise scales multiply the fp32 partial
@@ -62,7 +62,11 @@ struct Smem {
   uint32_t sb[2][BN];
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
+// 16-byte chunk c of LDS row r sits at position c ^ (r & 7) ^ ((r >> 3) & 1):
+// 16 consecutive rows read at one chunk cover all 64 LDS banks.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * BK + ((chunk ^ (row & 7) ^ ((row >> 3) & 1)) << 4);
+}
 
 // Load a (ROWS x 128) K tile of an operand into registers: ROWS*8 chunks of 16 B.
 template <int ROWS>

@@ -11,10 +11,10 @@
 //     32 B/clk/CU from L2, half of what a 128 x 128 tile needs.
 //   * Operands go global -> LDS directly (global_load_lds_dwordx4), without
 //     passing through VGPRs.  Such a load writes lane L's 16 bytes to LDS slot
-//     L of a 1 KB block, so the swizzled LDS layout (16-byte chunk c of row r
-//     at position c ^ (r & 7) of the row, which makes the 16-byte fragment
-//     reads of 8 consecutive rows conflict-free) is produced by choosing, per
-//     lane, which (row, chunk) of global memory it fetches.  Rows past M / N
+//     L of a 1 KB block, so the swizzled LDS layout (see row_swizzle: the
+//     16-byte fragment reads of 16 consecutive rows are conflict-free) is
+//     produced by choosing, per lane, which (row, chunk) of global memory it
+//     fetches.  Rows past M / N
 //     are clamped to the last row (their results are never stored).
 //   * Two LDS stages (2 x 64 KB): the loads of K tile t+1 are in flight while
 //     tile t is multiplied; one barrier per K tile.
@@ -55,6 +55,14 @@ struct FastArgs {
   int64_t tiles_m, tiles_n;
 };
 
+// 16-byte chunk c of LDS row r is stored at position c ^ row_swizzle(r).  A
+// fragment read has 16 lanes read 16 consecutive rows at one chunk; the LDS
+// serves a 16-lane group over 64 four-byte banks (256 B), and rows r and r+8
+// are 1 KB apart, i.e. on the same banks, so the swizzle flips bit 0 for the
+// second group of 8 rows: every 16-row group then covers all 64 banks, and
+// every 8-row group all 32 of the lower or upper half.
+__device__ __forceinline__ int row_swizzle(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
 // Byte offsets (from the operand base, without k0) of the chunks this thread
 // fetches for a ROWS-row tile: instruction i of wave w fills 1 KB block
 // i * 4 + w of the stage.
@@ -67,7 +75,7 @@ __device__ __forceinline__ void chunk_offsets(uint32_t (&off)[ROWS * CH / 256], 
     const int blk = i * 4 + wave;
     const int slot = blk * 64 + lane;
     const int row = slot / CH, pc = slot % CH;
-    const int c = pc ^ (row & 7);
+    const int c = pc ^ row_swizzle(row);
     int64_t gr = row0 + row;
     if (gr > nrows - 1) gr = nrows - 1;
     off[i] = (uint32_t)(gr * ld + c * 16);
@@ -206,7 +214,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
   // fragment addressing: lane half h reads chunks kk*4 + h and kk*4 + 2 + h
   const int a_row_off = (wm * WM + (lane & 31)) * FBK;
   const int b_row_off = (wn * WN + (lane & 31)) * FBK;
-  const int h = lane >> 5, x7 = lane & 7;
+  const int h = lane >> 5, x7 = row_swizzle(lane & 31);
   const int c00 = ((0 + h) ^ x7) << 4, c01 = ((2 + h) ^ x7) << 4;
   const int c10 = ((4 + h) ^ x7) << 4, c11 = ((6 + h) ^ x7) << 4;
   const int a_srow = wm * WM + (lane & 31), b_srow = wn * WN + (lane & 31);

@@ -115,6 +115,26 @@ __device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
   return v;
 }
 
+// Fold a workgroup's per-thread maxima (unsigned |x| bit patterns) into the
+// device-wide maximum at *out.  The workgroup reduces through LDS first and
+// only issues the device-scope atomic when its maximum exceeds the value it
+// reads at *out: thousands of workgroups would otherwise serialise on one
+// address.  A stale (smaller) read only costs an extra atomic, never a wrong
+// result.  Every thread of the workgroup must call this.
+template <int NTHREADS>
+__device__ __forceinline__ void block_max_to_global(uint32_t m, uint32_t* out, uint32_t* lds_scratch) {
+  m = wave_max_u32(m);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) lds_scratch[w] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < NTHREADS / 64; ++i) m = m > lds_scratch[i] ? m : lds_scratch[i];
+    if (m > 0x7F800000u) m = 0x7FC00000u;
+    const uint32_t cur = __hip_atomic_load(out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (m > cur) atomicMax(out, m);
+  }
+}
+
 // Per-tensor scale (recipe "tensorwise" and the --fp8-margin knob of the
 // "Low-Precision Training Guide"): scale = fp32(fmax / amax) * 2^-margin,
 // with amax == 0 or non-finite giving 1 and an overflowing quotient giving

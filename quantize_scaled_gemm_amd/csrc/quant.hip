@@ -145,11 +145,8 @@ __global__ __launch_bounds__(256) void amax_kernel(const In* __restrict__ x, int
       m = m > v ? m : v;
     }
   }
-  m = wave_max_u32(m);
-  if ((threadIdx.x & 63) == 0 && m != 0u) {
-    if (m > 0x7F800000u) m = 0x7FC00000u;
-    atomicMax(out, m);
-  }
+  __shared__ uint32_t red[4];
+  block_max_to_global<256>(m, out, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -410,10 +407,7 @@ __global__ __launch_bounds__(256) void tile_kernel(TileArgs a) {
   }
 
   if constexpr (MODE == MODE_TENSOR) {
-    if (a.amax_out) {
-      uint32_t m = wave_max_u32(amax_acc);
-      if ((tid & 63) == 0 && m != 0u) atomicMax(a.amax_out, canon(m));
-    }
+    if (a.amax_out) block_max_to_global<256>(amax_acc, a.amax_out, &lds_red[0][0]);
   }
 }
 
@@ -473,8 +467,8 @@ void launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
   }
   const bool vec_ok = ((uintptr_t)x % 16 == 0) && ((ld * esz) % 16 == 0);
   const int64_t vecs = vec_ok ? cols / (16 / esz) : cols;
-  int64_t gx = (vecs + 256 * 4 - 1) / (256 * 4);
-  const int64_t cap = (int64_t)num_cus() * 8;
+  int64_t gx = (vecs + 256 * 8 - 1) / (256 * 8);
+  const int64_t cap = (int64_t)num_cus() * 4;
   int64_t gy = rows;
   if (gx > cap) gx = cap;
   if (gx < 1) gx = 1;

@@ -270,46 +270,82 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
 #undef QSG_FAST_STEP
   __builtin_amdgcn_s_waitcnt(0);
 
-  // ---- epilogue ------------------------------------------------------------
+  // ---- epilogue: scale, convert, stage through LDS, coalesced stores -----
+  // Each wave owns a 128 x 128 block of C.  It writes a band of rows of that
+  // block into one of the (now idle) LDS stage buffers with a padded row
+  // stride (+8 bytes: the 32 rows a store instruction touches then land on
+  // distinct bank pairs), and stores the band back row by row with 16-byte
+  // lanes, so every store instruction writes whole 256- or 512-byte row
+  // segments instead of 16-byte pieces of 32 rows.
   float alpha = 1.0f;
   if constexpr (!MX) alpha = *reinterpret_cast<const float*>(g.sa) * *reinterpret_cast<const float*>(g.sb);
+  __syncthreads();  // every wave is done reading the LDS stages
+  constexpr int ESZ = OUT_BF16 ? 2 : 4;
+  constexpr int ROWB = WN * ESZ;          // bytes of one block row (256 or 512)
+  constexpr int STRIDE = ROWB + 8;        // padded LDS row stride
+  constexpr int BAND = OUT_BF16 ? 64 : 32;  // rows per pass (BAND * STRIDE <= 32 KB)
+  static_assert(BAND * STRIDE <= FBM * FBK, "band must fit a wave's LDS buffer");
+  uint8_t* band = (wave == 0) ? lds_a0 : (wave == 1) ? lds_a1 : (wave == 2) ? lds_b0 : lds_b1;
+  const int64_t bm0 = m0 + wm * WM, bn0 = n0 + wn * WN;
+  constexpr int LANES_PER_ROW = ROWB / 16;  // 16 (bf16) or 32 (fp32)
+  constexpr int ROWS_PER_INST = 64 / LANES_PER_ROW;
+  const int sl = lane % LANES_PER_ROW, sr = lane / LANES_PER_ROW;
 #pragma unroll
-  for (int i = 0; i < TMW; ++i) {
-    const int64_t m = m0 + wm * WM + i * 32 + (lane & 31);
-    if (m >= g.M) continue;
+  for (int pass = 0; pass < WM / BAND; ++pass) {
+    // acc tiles i with rows [i*32, i*32+32) inside this band
 #pragma unroll
-    for (int j = 0; j < TNW; ++j) {
+    for (int ii = 0; ii < BAND / 32; ++ii) {
+      const int i = pass * (BAND / 32) + ii;
+      const int r = ii * 32 + (lane & 31);
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const int64_t n = n0 + wn * WN + j * 32 + grp * 8 + (lane >> 5) * 4;
-        const float v0 = acc[i][j][grp * 4 + 0] * alpha, v1 = acc[i][j][grp * 4 + 1] * alpha;
-        const float v2 = acc[i][j][grp * 4 + 2] * alpha, v3 = acc[i][j][grp * 4 + 3] * alpha;
-        if constexpr (OUT_BF16) {
-          uint16_t* c = reinterpret_cast<uint16_t*>(g.c) + m * g.ldc + n;
-          const uint16_t h0 = f32_to_bf16_rne(v0), h1 = f32_to_bf16_rne(v1);
-          const uint16_t h2 = f32_to_bf16_rne(v2), h3 = f32_to_bf16_rne(v3);
-          if (g.vec_c && n + 3 < g.N) {
-            *reinterpret_cast<uint2*>(c) = make_uint2((uint32_t)h0 | ((uint32_t)h1 << 16),
-                                                      (uint32_t)h2 | ((uint32_t)h3 << 16));
+      for (int j = 0; j < TNW; ++j) {
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+          const int col = j * 32 + grp * 8 + (lane >> 5) * 4;
+          const float v0 = acc[i][j][grp * 4 + 0] * alpha, v1 = acc[i][j][grp * 4 + 1] * alpha;
+          const float v2 = acc[i][j][grp * 4 + 2] * alpha, v3 = acc[i][j][grp * 4 + 3] * alpha;
+          uint8_t* dst = band + r * STRIDE + col * ESZ;
+          if constexpr (OUT_BF16) {
+            *reinterpret_cast<uint2*>(dst) =
+                make_uint2((uint32_t)f32_to_bf16_rne(v0) | ((uint32_t)f32_to_bf16_rne(v1) << 16),
+                           (uint32_t)f32_to_bf16_rne(v2) | ((uint32_t)f32_to_bf16_rne(v3) << 16));
           } else {
-            if (n + 0 < g.N) c[0] = h0;
-            if (n + 1 < g.N) c[1] = h1;
-            if (n + 2 < g.N) c[2] = h2;
-            if (n + 3 < g.N) c[3] = h3;
-          }
-        } else {
-          float* c = reinterpret_cast<float*>(g.c) + m * g.ldc + n;
-          if (g.vec_c && n + 3 < g.N) {
-            *reinterpret_cast<float4*>(c) = make_float4(v0, v1, v2, v3);
-          } else {
-            if (n + 0 < g.N) c[0] = v0;
-            if (n + 1 < g.N) c[1] = v1;
-            if (n + 2 < g.N) c[2] = v2;
-            if (n + 3 < g.N) c[3] = v3;
+            *reinterpret_cast<uint2*>(dst) = make_uint2(__float_as_uint(v0), __float_as_uint(v1));
+            *reinterpret_cast<uint2*>(dst + 8) = make_uint2(__float_as_uint(v2), __float_as_uint(v3));
           }
         }
       }
     }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int rr = 0; rr < BAND; rr += ROWS_PER_INST) {
+      const int r = rr + sr;
+      const int64_t m = bm0 + pass * BAND + r;
+      const int64_t n = bn0 + sl * (16 / ESZ);
+      const uint8_t* src = band + r * STRIDE + sl * 16;
+      const uint2 lo = *reinterpret_cast<const uint2*>(src);
+      const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
+      if (m < g.M) {
+        uint8_t* cp = reinterpret_cast<uint8_t*>(g.c) + (m * g.ldc + n) * ESZ;
+        if (g.vec_c && n + 16 / ESZ <= g.N) {
+          *reinterpret_cast<uint4*>(cp) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        } else {
+          const uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+          for (int e = 0; e < 16 / ESZ; ++e) {
+            if (n + e < g.N) {
+              if constexpr (OUT_BF16)
+                reinterpret_cast<uint16_t*>(cp)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+              else
+                reinterpret_cast<uint32_t*>(cp)[e] = w[e];
+            }
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads of the band done before the next pass overwrites it
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -346,7 +382,8 @@ bool launch_scaled_gemm_fast(const uint8_t* a, int fa, bool mx, const void* sa, 
   g.a = a; g.b = b; g.sa = sa; g.sb = sb;
   g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.c = c;
   const bool out_bf16 = (c_dtype == 1);
-  g.vec_c = out_bf16 ? (((uintptr_t)c % 8 == 0) && (ldc % 4 == 0)) : (((uintptr_t)c % 16 == 0) && (ldc % 4 == 0));
+  // 16-byte row-segment stores need 16-byte aligned rows
+  g.vec_c = ((uintptr_t)c % 16 == 0) && ((ldc * (out_bf16 ? 2 : 4)) % 16 == 0);
   g.tiles_m = tiles_m;
   g.tiles_n = tiles_n;
   if (mx)

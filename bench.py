@@ -260,7 +260,7 @@ def main():
     if os.path.exists(prof_path):
         with open(prof_path) as fh:
             tr = json.load(fh).get(dom)
-        if tr and tr.get("source_hash") == source_hash("gemm.hip"):
+        if tr and tr.get("source_hash") == source_hash("gemm_fast.hip"):
             traffic = tr.get("bytes_per_launch")
 
     line = {

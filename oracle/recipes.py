@@ -235,12 +235,18 @@ def mx_quantize(x, fmt="e4m3", rule="ceil", margin=0, rowwise=True, colwise=True
 # blockwise (1 x 128 activations, 128 x 128 weights)
 # --------------------------------------------------------------------------
 def block_scale(block_amax, fmt, margin=0):
-    """Per-block (scale, scale_inv) arrays: R1/R2 applied to every block."""
+    """Per-block (scale, scale_inv) arrays: R1/R2 applied to every block,
+    element-wise (the same steps as ``tensorwise_scale``)."""
     a = np.ascontiguousarray(block_amax, dtype=np.float32)
-    s = np.empty_like(a)
-    si = np.empty_like(a)
-    for idx in np.ndindex(a.shape):
-        s[idx], si[idx] = tensorwise_scale(a[idx], fmt, margin)
+    fmax = np.float32(FORMATS[fmt]["max"])
+    degenerate = (a == 0) | ~np.isfinite(a)
+    with np.errstate(over="ignore", divide="ignore", invalid="ignore"):
+        q = (fmax / np.where(degenerate, np.float32(1), a)).astype(np.float32)
+    q = np.where(np.isinf(q), _FLT_MAX, q).astype(np.float32)
+    q = (q * np.float32(2.0 ** -margin)).astype(np.float32)
+    s = np.where(degenerate, np.float32(1.0), q).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        si = (np.float32(1.0) / s).astype(np.float32)
     return s, si
 
 

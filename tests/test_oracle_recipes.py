@@ -326,3 +326,16 @@ def test_block_dequant_error_bound(fmt):
     # the scale itself is rounded to binary32, so allow its relative error
     assert np.all(np.abs(dec - v) <= ulp / 2 + np.abs(v) * 2.0 ** -22)
     assert np.all(np.abs(dec) <= FORMATS[fmt]["max"])
+
+
+def test_block_scale_matches_tensorwise_scale_elementwise():
+    g = np.random.Generator(np.random.PCG64(24))
+    with np.errstate(over="ignore"):
+        a = np.exp(g.uniform(-100, 100, 4000)).astype(np.float32)  # includes inf
+    a = np.concatenate([a, np.float32([0.0, np.inf, np.nan, 1e-45, 448.0, 3e38])])
+    for fmt in ("e4m3", "e5m2"):
+        for margin in (0, 3):
+            s, si = oracle.block_scale(a, fmt, margin)
+            for k in range(a.size):
+                rs, rsi = oracle.tensorwise_scale(a[k], fmt, margin)
+                assert bits(s[k]) == bits(rs) and bits(si[k]) == bits(rsi), (a[k], fmt, margin)

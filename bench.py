@@ -140,6 +140,122 @@ def build_step(torch, q, dev):
     return step, step_flops, step_elems
 
 
+def time_fn(torch, fn, reps=10, warm=2):
+    """Average milliseconds of fn() over reps, HIP events on the current stream."""
+    for _ in range(warm):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def other_recipes(torch, q, dev):
+    """Kernel throughput of the delayed, MXFP8 and blockwise workloads (the
+    shapes of the parity tests), reported next to the headline step."""
+    import numpy as np
+
+    import workloads
+
+    def d(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    u8 = dict(dtype=torch.uint8, device=dev)
+    out = {}
+
+    # delayed scaling, Linear 4096 -> 4096, 8192 tokens: one step
+    st = workloads.delayed_4096_step(0)
+    X, dY = d(st["X"]), d(st["dY"])
+    W = d(workloads.delayed_4096_weight())
+    R, C = X.shape
+    bufs = {}
+    for n, t, f in (("X", X, q.E4M3), ("W", W, q.E4M3), ("dY", dY, q.E5M2)):
+        r, c = t.shape
+        bufs[n] = dict(x=t, f=f, q=torch.empty((r, c), **u8), qt=torch.empty((c, r), **u8),
+                       amax=torch.zeros(1, device=dev), scale=torch.ones(1, device=dev),
+                       sinv=torch.ones(1, device=dev), hist=torch.zeros(1024, device=dev))
+    Y = torch.empty((R, W.shape[0]), dtype=torch.bfloat16, device=dev)
+    dX = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
+    dW = torch.empty(W.shape, dtype=torch.bfloat16, device=dev)
+    T = q.DELAYED
+
+    def quant(n):
+        b = bufs[n]
+        q.qsg_cast_transpose(b["x"], b["f"], b["scale"], b["q"], b["qt"], b["amax"])
+        q.qsg_amax_update(b["hist"], 0, b["amax"], b["f"], 0, b["scale"], b["sinv"])
+
+    x, w, dy = bufs["X"], bufs["W"], bufs["dY"]
+    ms_q = time_fn(torch, lambda: [quant(n) for n in ("X", "W", "dY")])
+    ms_g = time_fn(torch, lambda: (
+        q.qsg_scaled_gemm(x["q"], q.E4M3, T, x["sinv"], w["q"], q.E4M3, T, w["sinv"], Y),
+        q.qsg_scaled_gemm(dy["q"], q.E5M2, T, dy["sinv"], w["qt"], q.E4M3, T, w["sinv"], dX),
+        q.qsg_scaled_gemm(dy["qt"], q.E5M2, T, dy["sinv"], x["qt"], q.E4M3, T, x["sinv"], dW)))
+    qbytes = 4.0 * (X.numel() + W.numel() + dY.numel())
+    gfl = 3 * gemm_flops(R, W.shape[0], C)
+    out["delayed_4096"] = {"quantize_ms": round(ms_q, 4), "quantize_GB/s": round(qbytes / ms_q / 1e6, 1),
+                           "gemm_ms": round(ms_g, 4), "gemm_TFLOP/s": round(gfl / ms_g / 1e9, 1),
+                           "step_ms": round(ms_q + ms_g, 4)}
+    del bufs, X, dY, W, Y, dX, dW
+
+    # MXFP8: X 16384x4096, W 14336x4096, dY 16384x14336
+    h = workloads.mxfp8_4096()
+    mx = {}
+    for n in ("X", "W", "dY"):
+        t = d(h[n])
+        r, c = t.shape
+        mx[n] = dict(x=t, q=torch.empty((r, c), **u8), s=torch.empty((r, c // 32), **u8),
+                     qt=torch.empty((c, r), **u8), st=torch.empty((c, r // 32), **u8))
+    del h
+
+    def mxq(n):
+        b = mx[n]
+        q.qsg_quantize(b["x"], q.MXFP8, q.E4M3, q=b["q"], s=b["s"], qt=b["qt"], st=b["st"])
+
+    ms_q = time_fn(torch, lambda: [mxq(n) for n in ("X", "W", "dY")])
+    x, w, dy = mx["X"], mx["W"], mx["dY"]
+    M, K = x["x"].shape
+    N = w["x"].shape[0]
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dW = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    X_ = q.MXFP8
+    ms_f = time_fn(torch, lambda: q.qsg_scaled_gemm(x["q"], q.E4M3, X_, x["s"], w["q"], q.E4M3, X_, w["s"], Y))
+    ms_d = time_fn(torch, lambda: q.qsg_scaled_gemm(dy["q"], q.E4M3, X_, dy["s"], w["qt"], q.E4M3, X_, w["st"], dX))
+    ms_w = time_fn(torch, lambda: q.qsg_scaled_gemm(dy["qt"], q.E4M3, X_, dy["st"], x["qt"], q.E4M3, X_, x["st"], dW))
+    qbytes = (4.0 + 2.0 / 32) * sum(mx[n]["x"].numel() for n in mx)
+    gf = gemm_flops(M, N, K)
+    out["mxfp8_4096"] = {"quantize_ms": round(ms_q, 4), "quantize_GB/s": round(qbytes / ms_q / 1e6, 1),
+                         "fprop_TFLOP/s": round(gf / ms_f / 1e9, 1), "dgrad_TFLOP/s": round(gf / ms_d / 1e9, 1),
+                         "wgrad_TFLOP/s": round(gf / ms_w / 1e9, 1),
+                         "step_ms": round(ms_q + ms_f + ms_d + ms_w, 4)}
+    del mx, Y, dX, dW
+
+    # blockwise: X 16384x7168 (1x128, row + column copies), W 18432x7168 (128x128)
+    h = workloads.blockwise_7168()
+    X, W = d(h["X"]), d(h["W"])
+    del h
+    M, K = X.shape
+    N = W.shape[0]
+    qx = dict(q=torch.empty((M, K), **u8), s=torch.empty((M, K // 128), device=dev),
+              qt=torch.empty((K, M), **u8), st=torch.empty((K, M // 128), device=dev))
+    qw = dict(q=torch.empty((N, K), **u8), s=torch.empty((N // 128, K // 128), device=dev),
+              qt=torch.empty((K, N), **u8), st=torch.empty((K // 128, N // 128), device=dev))
+    ms_qx = time_fn(torch, lambda: q.qsg_quantize(X, q.BLOCK_1X128, q.E4M3, **qx))
+    ms_qw = time_fn(torch, lambda: q.qsg_quantize(W, q.BLOCK_128X128, q.E4M3, **qw))
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ms_f = time_fn(torch, lambda: q.qsg_scaled_gemm(qx["q"], q.E4M3, q.BLOCK_1X128, qx["s"], qw["q"], q.E4M3,
+                                                    q.BLOCK_128X128, qw["s"], Y), reps=5)
+    out["blockwise_7168"] = {"quantize_act_ms": round(ms_qx, 4),
+                             "quantize_act_GB/s": round((4.0 + 8.0 / 128) * X.numel() / ms_qx / 1e6, 1),
+                             "quantize_weight_ms": round(ms_qw, 4),
+                             "quantize_weight_GB/s": round((4.0 + 8.0 / 16384) * W.numel() / ms_qw / 1e6, 1),
+                             "fprop_TFLOP/s": round(gemm_flops(M, N, K) / ms_f / 1e9, 1)}
+    return out
+
+
 def cpu_baseline(step_flops, step_elems):
     """The oracle, untuned, on a bounded sample of the same workload, scaled
     to the step's TFLOP/s."""
@@ -193,6 +309,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all-recipes", action="store_true",
+                    help="also time the delayed, MXFP8 and blockwise workloads (reported under 'recipes')")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy three times (the reference "
                          "kernel for scaling HBM byte counters)")
@@ -288,6 +406,8 @@ def main():
         "cast_transpose_frac": round(ct_gbps / PEAK_HBM_GBPS, 4),
         "kernels": kernels,
     }
+    if args.all_recipes:
+        line["recipes"] = other_recipes(torch, q, dev)
     if not args.no_cpu_baseline:
         t0 = time.time()
         line["cpu_baseline"] = cpu_baseline(step_flops, step_elems)

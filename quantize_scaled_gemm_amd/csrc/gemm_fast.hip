@@ -14,20 +14,27 @@
 //     L of a 1 KB block, so the swizzled LDS layout (see row_swizzle: the
 //     16-byte fragment reads of 16 consecutive rows are conflict-free) is
 //     produced by choosing, per lane, which (row, chunk) of global memory it
-//     fetches.  Rows past M / N
-//     are clamped to the last row (their results are never stored).
-//   * Two LDS stages (2 x 64 KB): the loads of K tile t+1 are in flight while
-//     tile t is multiplied; one barrier per K tile.
+//     fetches; every load instruction covers 8 whole 128-byte row segments.
+//     Rows past M / N are clamped to the last row (never stored).
+//   * Two LDS stages (2 x 64 KB).  The vector-memory path moves ~60 B/clk/CU,
+//     so a K tile's 64 KB occupies it for more than half of the tile's MFMA
+//     time: the fetch of tile t+2 is spread over the middle and last phase of
+//     tile t (three phases around two barriers per K tile, see the main
+//     loop) instead of being issued in a burst, which would stall the
+//     in-order wave behind a full load queue.
 //   * MXFP8: the 4 E8M0 bytes of a row for the tile's 4 K blocks travel with
 //     the tile (global_load_lds_dword); lane half h shifts its row's word by
 //     8h so that op_sel 0 / 2 pick the bytes of K blocks h / 2+h for the two
 //     64-K MFMA steps (the MFMA operand K order: lane half h holds K
 //     [16h, 16h+16) and [32+16h, 48+16h) of a step; the scale of lanes 0..31
 //     covers K 0..31 and that of lanes 32..63 covers K 32..63).
-//   * Tile order: workgroup ids are dispatched round-robin over the 8 XCDs;
-//     they are remapped so each XCD owns a contiguous range of tiles, walked
-//     in groups of 4 tile-rows x all tile-columns, so the 32 tiles an XCD runs
-//     at once share 4 A panels and 8 B panels in its L2.
+//   * Persistent workgroups, one per CU.  Workgroup ids are dispatched
+//     round-robin over the 8 XCDs; the workgroups of an XCD take turns over a
+//     contiguous range of the tile order, walked in groups of 4 tile-rows x
+//     all tile-columns, so the 32 tiles an XCD runs at once share 4 A panels
+//     and 8 B panels in its L2.  The next tile's first K tiles are fetched
+//     before the current tile's results are written out (through a separate
+//     LDS band), so that fetch overlaps the epilogue.
 #include <hip/hip_runtime.h>
 
 #include "qsg_device.h"
@@ -53,6 +60,7 @@ struct FastArgs {
   void* c;
   bool vec_c;
   int64_t tiles_m, tiles_n;
+  int64_t max_wgs;  // persistent grid: one workgroup per CU
 };
 
 // 16-byte chunk c of LDS row r is stored at position c ^ row_swizzle(r).  A
@@ -149,6 +157,39 @@ __device__ __forceinline__ void issue_stage(const FastArgs& g, const uint32_t (&
   }
 }
 
+// Half of a stage's fetch: part 0 = the A tile (+ MX scale words), part 1 = the B tile.
+template <int S, int PART>
+__device__ __forceinline__ void issue_part(const FastArgs& g, const uint32_t (&offa)[FBM * CH / 256],
+                                           const uint32_t (&offb)[FBN * CH / 256], const uint8_t* sa_row,
+                                           const uint8_t* sb_row, bool mx, int64_t kt) {
+  if constexpr (PART == 0) {
+    issue_tile<FBM>(g.a, offa, kt * FBK, stage_a<S>());
+    if (mx) {
+      const int wave = threadIdx.x >> 6;
+      __builtin_amdgcn_global_load_lds((const void*)(sa_row + kt * 4), (lds_ptr_t)(stage_sa<S>() + wave * 64), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(sb_row + kt * 4), (lds_ptr_t)(stage_sb<S>() + wave * 64), 4, 0, 0);
+    }
+  } else {
+    issue_tile<FBN>(g.b, offb, kt * FBK, stage_b<S>());
+  }
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier without a memory fence (a fence would also wait for the
+// global->LDS loads in flight); the waits it needs are explicit.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+
 template <int S, bool MX>
 __device__ __forceinline__ void load_frags(Frags& f, int kk, int a_row_off, int b_row_off, int c_lo, int c_hi,
                                            int a_srow, int b_srow, int sh) {
@@ -164,18 +205,38 @@ __device__ __forceinline__ void load_frags(Frags& f, int kk, int a_row_off, int 
   }
 }
 
-template <bool MX, int FA, int FB>
-__device__ __forceinline__ void mfma_block(v16f (&acc)[TMW][TNW], const Frags& f) {
+// MFMAs LO..HI-1 of one 64-K step, MFMA q updating accumulator tile
+// (q / TNW, q % TNW).
+template <bool MX, int FA, int FB, int LO, int HI>
+__device__ __forceinline__ void mfma_range(v16f (&acc)[TMW][TNW], const Frags& f) {
 #pragma unroll
-  for (int i = 0; i < TMW; ++i) {
-#pragma unroll
-    for (int j = 0; j < TNW; ++j) {
-      if constexpr (MX)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, 0, f.sb[j], 0, f.sa[i]);
-      else
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, 0, 0, 0, 0);
-    }
+  for (int q = LO; q < HI; ++q) {
+    const int i = q / TNW, j = q % TNW;
+    if constexpr (MX)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, 0, f.sb[j], 0, f.sa[i]);
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, 0, 0, 0, 0);
   }
+}
+
+// Epilogue staging: per wave a band of 32 rows x 128 bytes of C, with a
+// padded row stride (bf16 136 B, fp32 144 B) that keeps the accumulator
+// writes (8 or 16 bytes for 32 rows at one column) free of bank conflicts.
+// It lives outside the operand stages, so the next tile's operands can be
+// fetched while the band is written out.
+constexpr int EPI_STRIDE_MAX = 144;
+__shared__ __attribute__((aligned(256))) uint8_t lds_c[4][32 * EPI_STRIDE_MAX];
+
+// Tile t of the XCD-aware order: workgroup ids are dispatched round-robin
+// over the 8 XCDs, each XCD owns a contiguous range of the logical tile
+// order, walked in groups of 4 tile-rows x all tile-columns.
+__device__ __forceinline__ void tile_coords(const FastArgs& g, int64_t logical, int64_t& m0, int64_t& n0) {
+  constexpr int64_t GM = 4;
+  const int64_t per_group = GM * g.tiles_n;
+  const int64_t first_m = (logical / per_group) * GM;
+  const int64_t gsize = (g.tiles_m - first_m) < GM ? (g.tiles_m - first_m) : GM;
+  m0 = (first_m + (logical % per_group) % gsize) * FBM;
+  n0 = ((logical % per_group) / gsize) * FBN;
 }
 
 template <bool MX, int FA, int FB, bool OUT_BF16>
@@ -184,33 +245,19 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // tile coordinates: XCD-contiguous ranges, groups of 4 tile-rows
+  // Persistent workgroups: the ones on XCD x (ids x, x+8, ...) take turns
+  // over XCD x's contiguous range of logical tiles.
   const int64_t T = g.tiles_m * g.tiles_n;
-  const int64_t bid = blockIdx.x;
-  const int64_t xcd = bid % 8, local = bid / 8;
+  const int64_t G = gridDim.x;
+  const int64_t xcd = blockIdx.x % 8, local = blockIdx.x / 8;
   const int64_t per = T / 8, rem = T % 8;
-  const int64_t logical = xcd * per + (xcd < rem ? xcd : rem) + local;
-  constexpr int64_t GM = 4;
-  const int64_t per_group = GM * g.tiles_n;
-  const int64_t first_m = (logical / per_group) * GM;
-  const int64_t gsize = (g.tiles_m - first_m) < GM ? (g.tiles_m - first_m) : GM;
-  const int64_t m0 = (first_m + (logical % per_group) % gsize) * FBM;
-  const int64_t n0 = ((logical % per_group) / gsize) * FBN;
+  const int64_t x_begin = xcd * per + (xcd < rem ? xcd : rem);
+  const int64_t x_end = x_begin + per + (xcd < rem ? 1 : 0);
+  const int64_t x_wgs = G / 8 + (xcd < G % 8 ? 1 : 0);
+  int64_t logical = x_begin + local;
+  if (logical >= x_end) return;
   const int64_t nk = g.K / FBK;  // even (checked by the launcher)
 
-  uint32_t offa[FBM * CH / 256], offb[FBN * CH / 256];
-  chunk_offsets<FBM>(offa, m0, g.M, g.lda);
-  chunk_offsets<FBN>(offb, n0, g.N, g.ldb);
-  const uint8_t* sa_row = nullptr;
-  const uint8_t* sb_row = nullptr;
-  if constexpr (MX) {
-    const int64_t nb = g.K / 32;
-    int64_t ra = m0 + threadIdx.x, rb = n0 + threadIdx.x;
-    if (ra > g.M - 1) ra = g.M - 1;
-    if (rb > g.N - 1) rb = g.N - 1;
-    sa_row = reinterpret_cast<const uint8_t*>(g.sa) + ra * nb;
-    sb_row = reinterpret_cast<const uint8_t*>(g.sb) + rb * nb;
-  }
   // fragment addressing: lane half h reads chunks kk*4 + h and kk*4 + 2 + h
   const int a_row_off = (wm * WM + (lane & 31)) * FBK;
   const int b_row_off = (wn * WN + (lane & 31)) * FBK;
@@ -220,138 +267,202 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
   const int a_srow = wm * WM + (lane & 31), b_srow = wn * WN + (lane & 31);
   // MX: bytes h (first 64-K step) and 2 + h (second) of the row's word
   const int sh0 = 8 * h, sh1 = 8 * h + 16;
+  float alpha = 1.0f;
+  if constexpr (!MX) alpha = *reinterpret_cast<const float*>(g.sa) * *reinterpret_cast<const float*>(g.sb);
 
-  v16f acc[TMW][TNW];
-#pragma unroll
-  for (int i = 0; i < TMW; ++i)
-#pragma unroll
-    for (int j = 0; j < TNW; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  Frags f0, f1;
+  int64_t m0, n0;
+  tile_coords(g, logical, m0, n0);
+  uint32_t offa[FBM * CH / 256], offb[FBN * CH / 256];
+  const uint8_t* sa_row = nullptr;
+  const uint8_t* sb_row = nullptr;
+  auto tile_setup = [&]() {
+    chunk_offsets<FBM>(offa, m0, g.M, g.lda);
+    chunk_offsets<FBN>(offb, n0, g.N, g.ldb);
+    if constexpr (MX) {
+      const int64_t nb = g.K / 32;
+      int64_t ra = m0 + threadIdx.x, rb = n0 + threadIdx.x;
+      if (ra > g.M - 1) ra = g.M - 1;
+      if (rb > g.N - 1) rb = g.N - 1;
+      sa_row = reinterpret_cast<const uint8_t*>(g.sa) + ra * nb;
+      sb_row = reinterpret_cast<const uint8_t*>(g.sb) + rb * nb;
+    }
+  };
+  constexpr int P1 = 9, P2 = 7;
+  constexpr int NA = FBM * CH / 256 + (MX ? 2 : 0);  // fetches in a part-0 issue
+  constexpr int NS = 2 * (FBM * CH / 256) + (MX ? 2 : 0);  // fetches of a whole stage
+  constexpr int NSTORE = (OUT_BF16 ? 32 : 64);  // epilogue stores per wave
+  tile_setup();
   issue_stage<0>(g, offa, offb, sa_row, sb_row, MX, 0);
   issue_stage<1>(g, offa, offb, sa_row, sb_row, MX, 1);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  load_frags<0, MX>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);
+  wait_vm_lgkm0<NS>();  // stage 0 landed
 
-  // One K tile in stage S (f0 holds its first 64-K fragments on entry): the
-  // second-step fragments are read while the first-step MFMAs run; after the
-  // barrier the tile two ahead is fetched into stage S and the next tile's
-  // first-step fragments are read from stage S^1 while the second-step MFMAs
-  // run.  Past the last tile the fetch repeats the last tile and the reads
-  // are unused, which keeps the body branch-free.
+  v16f acc[TMW][TNW];
+  Frags f0, f1;
+  while (true) {
+#pragma unroll
+    for (int i = 0; i < TMW; ++i)
+#pragma unroll
+      for (int j = 0; j < TNW; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    lds_barrier();  // stage 0 is complete for every wave
+    load_frags<0, MX>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);
+
+  // One K tile KT in stage S (f0 holds its first 64-K fragments), in three
+  // phases around two barriers:
+  //   1. MFMAs 0..P1-1 of f0; the second-step fragments f1 are read from S.
+  //   2. barrier (every wave is done reading S); MFMAs P1..15 of f0 and
+  //      0..P2-1 of f1; the A half of tile KT+2 is fetched into S.
+  //   3. wait for this wave's fetches of tile KT+1, barrier (tile KT+1 is
+  //      complete in S^1); MFMAs P2..15 of f1; the first-step fragments of
+  //      KT+1 are read from S^1 and the B half of KT+2 is fetched into S.
+  // The fetch of a tile is spread over phases 2 and 3 and has until phase 3
+  // of the next step to land.  Past the last tile the fetch repeats the last
+  // tile and is unused, which keeps the body branch-free.
 #define QSG_FAST_STEP(S, KT)                                                                   \
   {                                                                                            \
     load_frags<S, MX>(f1, 1, a_row_off, b_row_off, c10, c11, a_srow, b_srow, sh1);             \
-    mfma_block<MX, FA, FB>(acc, f0);                                                           \
-    _Pragma("unroll") for (int q = 0; q < TMW * TNW; ++q) {                                    \
+    mfma_range<MX, FA, FB, 0, P1>(acc, f0);                                                    \
+    _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                            \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                       \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                       \
     }                                                                                          \
-    __builtin_amdgcn_s_waitcnt(0);                                                             \
-    __syncthreads();                                                                           \
+    __builtin_amdgcn_sched_group_barrier(0x008, P1 - 8, 0);                                    \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
+    wait_vm_lgkm0<63>();                                                                       \
+    lds_barrier();                                                                             \
     const int64_t nxt = (KT) + 2 < nk ? (KT) + 2 : nk - 1;                                     \
-    issue_stage<S>(g, offa, offb, sa_row, sb_row, MX, nxt);                                    \
-    load_frags<S ^ 1, MX>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);         \
-    mfma_block<MX, FA, FB>(acc, f1);                                                           \
-    _Pragma("unroll") for (int q = 0; q < TMW * TNW; ++q) {                                    \
+    issue_part<S, 0>(g, offa, offb, sa_row, sb_row, MX, nxt);                                  \
+    mfma_range<MX, FA, FB, P1, 16>(acc, f0);                                                   \
+    mfma_range<MX, FA, FB, 0, P2>(acc, f1);                                                    \
+    _Pragma("unroll") for (int q = 0; q < NA; ++q) {                                           \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);                                       \
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);                                       \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);                                       \
     }                                                                                          \
+    __builtin_amdgcn_sched_group_barrier(0x008, 16 - P1 + P2 - NA, 1);                         \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
+    wait_vm_lgkm0<NA>();                                                                       \
+    lds_barrier();                                                                             \
+    load_frags<S ^ 1, MX>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);         \
+    issue_part<S, 1>(g, offa, offb, sa_row, sb_row, MX, nxt);                                  \
+    mfma_range<MX, FA, FB, P2, 16>(acc, f1);                                                   \
+    _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                            \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);                                       \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);                                       \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 2);                                       \
+    }                                                                                          \
+    __builtin_amdgcn_sched_group_barrier(0x008, 16 - P2 - 8, 2);                               \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
   }
 
-  for (int64_t kt = 0; kt < nk; kt += 2) {
-    QSG_FAST_STEP(0, kt)
-    QSG_FAST_STEP(1, kt + 1)
-  }
-#undef QSG_FAST_STEP
-  __builtin_amdgcn_s_waitcnt(0);
-
-  // ---- epilogue: scale, convert, stage through LDS, coalesced stores -----
-  // Each wave owns a 128 x 128 block of C.  It writes a band of rows of that
-  // block into one of the (now idle) LDS stage buffers with a padded row
-  // stride (+8 bytes: the 32 rows a store instruction touches then land on
-  // distinct bank pairs), and stores the band back row by row with 16-byte
-  // lanes, so every store instruction writes whole 256- or 512-byte row
-  // segments instead of 16-byte pieces of 32 rows.
-  float alpha = 1.0f;
-  if constexpr (!MX) alpha = *reinterpret_cast<const float*>(g.sa) * *reinterpret_cast<const float*>(g.sb);
-  __syncthreads();  // every wave is done reading the LDS stages
-  constexpr int ESZ = OUT_BF16 ? 2 : 4;
-  constexpr int ROWB = WN * ESZ;          // bytes of one block row (256 or 512)
-  constexpr int STRIDE = ROWB + 8;        // padded LDS row stride
-  constexpr int BAND = OUT_BF16 ? 64 : 32;  // rows per pass (BAND * STRIDE <= 32 KB)
-  static_assert(BAND * STRIDE <= FBM * FBK, "band must fit a wave's LDS buffer");
-  uint8_t* band = (wave == 0) ? lds_a0 : (wave == 1) ? lds_a1 : (wave == 2) ? lds_b0 : lds_b1;
-  const int64_t bm0 = m0 + wm * WM, bn0 = n0 + wn * WN;
-  constexpr int LANES_PER_ROW = ROWB / 16;  // 16 (bf16) or 32 (fp32)
-  constexpr int ROWS_PER_INST = 64 / LANES_PER_ROW;
-  const int sl = lane % LANES_PER_ROW, sr = lane / LANES_PER_ROW;
-#pragma unroll
-  for (int pass = 0; pass < WM / BAND; ++pass) {
-    // acc tiles i with rows [i*32, i*32+32) inside this band
-#pragma unroll
-    for (int ii = 0; ii < BAND / 32; ++ii) {
-      const int i = pass * (BAND / 32) + ii;
-      const int r = ii * 32 + (lane & 31);
-#pragma unroll
-      for (int j = 0; j < TNW; ++j) {
-#pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-          const int col = j * 32 + grp * 8 + (lane >> 5) * 4;
-          const float v0 = acc[i][j][grp * 4 + 0] * alpha, v1 = acc[i][j][grp * 4 + 1] * alpha;
-          const float v2 = acc[i][j][grp * 4 + 2] * alpha, v3 = acc[i][j][grp * 4 + 3] * alpha;
-          uint8_t* dst = band + r * STRIDE + col * ESZ;
-          if constexpr (OUT_BF16) {
-            *reinterpret_cast<uint2*>(dst) =
-                make_uint2((uint32_t)f32_to_bf16_rne(v0) | ((uint32_t)f32_to_bf16_rne(v1) << 16),
-                           (uint32_t)f32_to_bf16_rne(v2) | ((uint32_t)f32_to_bf16_rne(v3) << 16));
-          } else {
-            *reinterpret_cast<uint2*>(dst) = make_uint2(__float_as_uint(v0), __float_as_uint(v1));
-            *reinterpret_cast<uint2*>(dst + 8) = make_uint2(__float_as_uint(v2), __float_as_uint(v3));
-          }
-        }
-      }
+    for (int64_t kt = 0; kt < nk; kt += 2) {
+      QSG_FAST_STEP(0, kt)
+      QSG_FAST_STEP(1, kt + 1)
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-    __builtin_amdgcn_wave_barrier();
+#undef QSG_FAST_STEP
+    // every wave is done with the operand stages
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+
+    // next tile: fetch its first two K tiles now, so that they land while
+    // this tile's results are written out
+    const int64_t cm0 = m0, cn0 = n0;
+    logical += x_wgs;
+    const bool more = logical < x_end;
+    if (more) {
+      tile_coords(g, logical, m0, n0);
+      tile_setup();
+      issue_stage<0>(g, offa, offb, sa_row, sb_row, MX, 0);
+    }
+
+    // ---- epilogue: scale, convert, stage through LDS, coalesced stores ----
+    // Each wave owns a 128 x 128 block of C, written as bands of 32 rows x
+    // 128 bytes: the accumulators go to the wave's LDS band, then every store
+    // instruction writes 8 whole 128-byte row segments.
+    constexpr int ESZ = OUT_BF16 ? 2 : 4;
+    constexpr int STRIDE = OUT_BF16 ? 136 : 144;
+    constexpr int BCOLS = 128 / ESZ;  // columns per band
+    constexpr int JPB = BCOLS / 32;   // accumulator column tiles per band
+    uint8_t* band = lds_c[wave];
+    const int64_t bm0 = cm0 + wm * WM, bn0 = cn0 + wn * WN;
+    const int sl = lane % 8, sr = lane / 8;
 #pragma unroll
-    for (int rr = 0; rr < BAND; rr += ROWS_PER_INST) {
-      const int r = rr + sr;
-      const int64_t m = bm0 + pass * BAND + r;
-      const int64_t n = bn0 + sl * (16 / ESZ);
-      const uint8_t* src = band + r * STRIDE + sl * 16;
-      const uint2 lo = *reinterpret_cast<const uint2*>(src);
-      const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
-      if (m < g.M) {
-        uint8_t* cp = reinterpret_cast<uint8_t*>(g.c) + (m * g.ldc + n) * ESZ;
-        if (g.vec_c && n + 16 / ESZ <= g.N) {
-          *reinterpret_cast<uint4*>(cp) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        } else {
-          const uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
+    for (int i = 0; i < TMW; ++i) {
 #pragma unroll
-          for (int e = 0; e < 16 / ESZ; ++e) {
-            if (n + e < g.N) {
-              if constexpr (OUT_BF16)
-                reinterpret_cast<uint16_t*>(cp)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-              else
-                reinterpret_cast<uint32_t*>(cp)[e] = w[e];
+      for (int jb = 0; jb < TNW / JPB; ++jb) {
+        const int r = lane & 31;
+#pragma unroll
+        for (int jj = 0; jj < JPB; ++jj) {
+          const int j = jb * JPB + jj;
+#pragma unroll
+          for (int grp = 0; grp < 4; ++grp) {
+            const int col = jj * 32 + grp * 8 + (lane >> 5) * 4;
+            const float v0 = acc[i][j][grp * 4 + 0] * alpha, v1 = acc[i][j][grp * 4 + 1] * alpha;
+            const float v2 = acc[i][j][grp * 4 + 2] * alpha, v3 = acc[i][j][grp * 4 + 3] * alpha;
+            uint8_t* dst = band + r * STRIDE + col * ESZ;
+            if constexpr (OUT_BF16) {
+              *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+            } else {
+              *reinterpret_cast<uint4*>(dst) =
+                  make_uint4(__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2), __float_as_uint(v3));
             }
           }
         }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's band writes are done
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int rr = 0; rr < 32; rr += 8) {
+          const int rw = rr + sr;
+          const int64_t m = bm0 + i * 32 + rw;
+          const int64_t n = bn0 + jb * BCOLS + sl * (16 / ESZ);
+          const uint4 v = *reinterpret_cast<const uint4*>(band + rw * STRIDE + sl * 16);
+          if (m < g.M) {
+            uint8_t* cp = reinterpret_cast<uint8_t*>(g.c) + (m * g.ldc + n) * ESZ;
+            if (g.vec_c && n + 16 / ESZ <= g.N) {
+              *reinterpret_cast<uint4*>(cp) = v;
+            } else {
+              const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+              for (int e = 0; e < 16 / ESZ; ++e) {
+                if (n + e < g.N) {
+                  if constexpr (OUT_BF16)
+                    reinterpret_cast<uint16_t*>(cp)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                  else
+                    reinterpret_cast<uint32_t*>(cp)[e] = w[e];
+                }
+              }
+            }
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // band reads done before the next band overwrites it
+        __builtin_amdgcn_wave_barrier();
       }
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads of the band done before the next pass overwrites it
-    __builtin_amdgcn_wave_barrier();
+    if (!more) break;
+    // The stores are in flight; stage 1 is fetched behind them, and only
+    // stage 0 is waited for here (the stores must have landed by the first
+    // wait for stage 1, in the next tile's first step).
+    issue_stage<1>(g, offa, offb, sa_row, sb_row, MX, 1);
+    wait_vm_lgkm0<(NSTORE + NS < 63 ? NSTORE + NS : 63)>();
   }
+}
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 template <bool MX, int FA, int FB>
 void launch_fast_cfg(const FastArgs& g, bool out_bf16, hipStream_t st) {
-  const unsigned grid = (unsigned)(g.tiles_m * g.tiles_n);
+  const int64_t tiles = g.tiles_m * g.tiles_n;
+  const unsigned grid = (unsigned)(tiles < g.max_wgs ? tiles : g.max_wgs);
   if (out_bf16)
     hipLaunchKernelGGL((gemm_fast_kernel<MX, FA, FB, true>), dim3(grid), dim3(256), 0, st, g);
   else
@@ -386,6 +497,7 @@ bool launch_scaled_gemm_fast(const uint8_t* a, int fa, bool mx, const void* sa, 
   g.vec_c = ((uintptr_t)c % 16 == 0) && ((ldc * (out_bf16 ? 2 : 4)) % 16 == 0);
   g.tiles_m = tiles_m;
   g.tiles_n = tiles_n;
+  g.max_wgs = device_cu_count();
   if (mx)
     launch_fast_fmt<true>(g, fa, fb, out_bf16, st);
   else

@@ -84,6 +84,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two binary32 values rounded to bfloat16 (round to nearest even) and packed,
+// `lo` in the low half: a single v_cvt_pk_bf16_f32 on gfx950.
+typedef float qsg_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 qsg_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const qsg_f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, qsg_bf16x2));
+}
+
 // |x| of a binary32 bit pattern; NaNs become the canonical 0x7FC00000 so
 // that an integer max over |x| patterns is order-free and reports NaN as
 // 0x7FC00000 (NaN > +inf > finite as unsigned integers).

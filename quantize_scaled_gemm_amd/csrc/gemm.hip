@@ -347,6 +347,11 @@ void launch_scaled_gemm(const uint8_t* a, int fa, int ka, const void* sa, const 
   if ((per_tensor || ka == 2) &&
       launch_scaled_gemm_fast(a, fa, ka == 2, sa, b, fb, sb, M, N, K, lda, ldb, c, c_dtype, ldc, st))
     return;
+  if (ka == 3 && kb == 4 &&
+      launch_scaled_gemm_block_fast(a, fa, reinterpret_cast<const float*>(sa), b, fb,
+                                    reinterpret_cast<const float*>(sb), true, M, N, K, lda, ldb, c, c_dtype, ldc,
+                                    st))
+    return;
   constexpr int BM = 128, BN = 128;
   GemmArgs g{};
   g.a = a; g.b = b; g.sa = sa; g.sb = sb;

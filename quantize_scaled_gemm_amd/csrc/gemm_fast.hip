@@ -439,11 +439,17 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
       }
     }
     if (!more) break;
-    // The stores are in flight; stage 1 is fetched behind them, and only
-    // stage 0 is waited for here (the stores must have landed by the first
-    // wait for stage 1, in the next tile's first step).
+    // The stores are in flight; stage 1 is fetched behind them.  For a tile
+    // inside the matrix every lane stores every segment, so exactly NSTORE
+    // store instructions are younger than stage 0 and it alone is waited
+    // for (the stores must land by the first wait for stage 1, in the next
+    // tile's first step).  An edge tile skips or splits stores, so there
+    // the wait also covers its stores.
     issue_stage<1>(g, offa, offb, sa_row, sb_row, MX, 1);
-    wait_vm_lgkm0<(NSTORE + NS < 63 ? NSTORE + NS : 63)>();
+    if (g.vec_c && cm0 + FBM <= g.M && cn0 + FBN <= g.N)
+      wait_vm_lgkm0<(NSTORE + NS < 63 ? NSTORE + NS : 63)>();
+    else
+      wait_vm_lgkm0<NS>();
   }
 }
 

@@ -267,3 +267,54 @@ def test_mx_adversarial_scales_error_bound(q):
     err = np.abs(y - ref)
     assert np.all(err <= 1e-2 * np.abs(ref) + 2.0 ** -10 * absref)
     assert np.linalg.norm(y - ref) / np.linalg.norm(ref) < 1e-3
+
+
+# ---------------------------------------------------------------------------
+# the blockwise path with 128 x 128 weight blocks (128 x 128 tiles, two
+# workgroups per CU; used when K % 256 == 0 and there are >= 512 tiles)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("fa,out", [(0, "f32"), (1, "bf16")])
+def test_block_fast_matches_row_slices(q, fa, out):
+    """Every output element is computed the same way by the large blockwise
+    path and by the general kernel (MFMA partial sum of each 128-K block,
+    then one fma with sa * sb), so the full problem (large path) must equal,
+    bit for bit, the same rows computed as 128-row slices (too few tiles for
+    the large path)."""
+    import torch
+
+    M, N, K = 2048 + 64, 4096 - 64, 512  # ragged M and N
+    g = workloads.generator(50, fa)
+    qa = rand_codes(g, (M, K), FMT_NAMES[fa])
+    qb = rand_codes(g, (N, K), "e4m3")
+    sa = g.uniform(1e-3, 1e-1, (M, K // 128)).astype(np.float32)
+    sb = g.uniform(1e-3, 1e-1, ((N + 127) // 128, K // 128)).astype(np.float32)
+    da, db, dsa, dsb = to_dev(qa), to_dev(qb), to_dev(sa), to_dev(sb)
+    full = gemm(q, da, fa, 3, dsa, db, 0, 4, dsb, out=out)
+    parts = []
+    for r0 in range(0, M, 128):
+        r1 = min(M, r0 + 128)
+        parts.append(gemm(q, da[r0:r1].contiguous(), fa, 3, dsa[r0:r1].contiguous(), db, 0, 4, dsb, out=out))
+    sliced = np.concatenate(parts, axis=0)
+    assert np.isfinite(full).all()
+    assert np.array_equal(full, sliced)
+    ref = oracle.gemm_block(qa[:256], FMT_NAMES[fa], sa[:256], qb, "e4m3", sb, "128x128")
+    ok, info = oracle.tolerance_check(full[:256], ref)
+    assert ok, info
+    del torch
+
+
+def test_block_fast_wide_scales(q):
+    """Blockwise scales spread over 12 binades per block and ragged N: the
+    large path against the fp64 oracle on a 256-row band."""
+    M, N, K = 4096, 2048 + 100, 768
+    g = workloads.generator(51)
+    qa = rand_codes(g, (M, K), "e4m3")
+    qb = rand_codes(g, (N, K), "e4m3")
+    sa = np.exp2(g.uniform(-20, -8, (M, K // 128))).astype(np.float32)
+    sb = np.exp2(g.uniform(-20, -8, ((N + 127) // 128, K // 128))).astype(np.float32)
+    y = gemm(q, to_dev(qa), 0, 3, to_dev(sa), to_dev(qb), 0, 4, to_dev(sb), out="f32")
+    rows = slice(1024, 1280)
+    ref = oracle.gemm_block(qa[rows], "e4m3", sa[rows], qb, "e4m3", sb, "128x128")
+    ok, info = oracle.tolerance_check(y[rows], ref)
+    assert ok, info
+    assert np.isfinite(y).all()

@@ -220,13 +220,13 @@ __global__ __launch_bounds__(256, 2) void gemm_block_kernel(BlockArgs g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // tile coordinates: XCD-contiguous ranges, groups of 8 tile-rows
+  // tile coordinates: XCD-contiguous ranges, groups of 4 tile-rows
   const int64_t T = g.tiles_m * g.tiles_n;
   const int64_t bid = blockIdx.x;
   const int64_t xcd = bid % 8, local = bid / 8;
   const int64_t per = T / 8, rem = T % 8;
   const int64_t logical = xcd * per + (xcd < rem ? xcd : rem) + local;
-  constexpr int64_t GM = 8;
+  constexpr int64_t GM = 4;
   const int64_t per_group = GM * g.tiles_n;
   const int64_t first_m = (logical / per_group) * GM;
   const int64_t gsize = (g.tiles_m - first_m) < GM ? (g.tiles_m - first_m) : GM;
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256, 2) void gemm_block_kernel(BlockArgs g) {
     sr.sa_row = g.sa + ra * nk;
     sr.sb_row = g.sb + (n0 / 128) * nk;
   }
-  constexpr int P1 = 3, P2 = 3;  // MFMA split of the three phases (8 per K block)
+  constexpr int P1 = 2, P2 = 4;  // MFMA split of the three phases (8 per K block)
   constexpr int NA = NCA + 2;    // fetch instructions of a part-0 issue
   constexpr int NS = NCA + NCB + 2;
   issue_stage<0>(g, offa, offb, sr, 0);

@@ -318,3 +318,38 @@ def test_block_fast_wide_scales(q):
     ok, info = oracle.tolerance_check(y[rows], ref)
     assert ok, info
     assert np.isfinite(y).all()
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_large_tile_persistent_edge_tiles(q, out):
+    """More tiles than CUs with a ragged last tile-row and tile-column: each
+    persistent workgroup runs several tiles, some of them edge tiles whose
+    epilogue skips rows and splits stores before the next tile starts.
+    Integer-valued operands make the result exact in binary32."""
+    M, N, K = 4096 + 100, 8192 + 40, 512
+    g = workloads.generator(52)
+    ia = g.integers(-15, 16, (M, K))
+    ib = g.integers(-15, 16, (N, K))
+    qa = oracle.encode(ia.astype(np.float32), "e4m3")
+    qb = oracle.encode(ib.astype(np.float32), "e4m3")
+    exact = ia.astype(np.float64) @ ib.T.astype(np.float64)
+    y = gemm(q, to_dev(qa), 0, 0, dscal(1.0), to_dev(qb), 0, 0, dscal(1.0), out=out)
+    want = exact if out == "f32" else f32_to_bf16_rne_f64(exact)
+    assert np.array_equal(y, want)
+
+
+def test_large_tile_mx_persistent_edge_tiles(q):
+    """MXFP8 through the persistent path with ragged M and N and several
+    tiles per workgroup: power-of-two block scales on integer codes keep every
+    product and partial sum exact, so the result is exact."""
+    M, N, K = 4096 + 72, 8192 + 24, 512
+    g = workloads.generator(53)
+    ia = g.integers(-8, 9, (M, K))
+    ib = g.integers(-8, 9, (N, K))
+    qa = oracle.encode(ia.astype(np.float32), "e4m3")
+    qb = oracle.encode(ib.astype(np.float32), "e4m3")
+    ea = g.integers(125, 130, (M, K // 32)).astype(np.uint8)  # 2^-2 .. 2^2
+    eb = g.integers(125, 130, (N, K // 32)).astype(np.uint8)
+    ref = oracle.gemm_mx(qa, "e4m3", ea, qb, "e4m3", eb)
+    y = gemm(q, to_dev(qa), 0, q.MXFP8, to_dev(ea), to_dev(qb), 0, q.MXFP8, to_dev(eb), out="f32")
+    assert np.array_equal(y, ref)

@@ -9,13 +9,14 @@
 //     (256 fp32 accumulators per lane).  At this tile size a workgroup needs
 //     64 KB of operand data per 128-K step for 2048 MFMA cycles per SIMD, i.e.
 //     32 B/clk/CU from L2, half of what a 128 x 128 tile needs.
-//   * Operands go global -> LDS directly (global_load_lds_dwordx4), without
-//     passing through VGPRs.  Such a load writes lane L's 16 bytes to LDS slot
-//     L of a 1 KB block, so the swizzled LDS layout (see row_swizzle: the
-//     16-byte fragment reads of 16 consecutive rows are conflict-free) is
-//     produced by choosing, per lane, which (row, chunk) of global memory it
-//     fetches; every load instruction covers 8 whole 128-byte row segments.
-//     Rows past M / N are clamped to the last row (never stored).
+//   * Operands go global -> LDS directly (buffer_load_dwordx4 ... lds),
+//     without passing through VGPRs.  Such a load writes lane L's 16 bytes to
+//     LDS slot L of a 1 KB block, so the swizzled LDS layout (see
+//     row_swizzle: the 16-byte fragment reads of 16 consecutive rows are
+//     conflict-free) is produced by choosing, per lane, which (row, chunk) of
+//     global memory it fetches; every load instruction covers 8 whole
+//     128-byte row segments.  The buffer resource of a tile ends at the
+//     matrix's last row, so rows past M / N read as zero (never stored).
 //   * Two LDS stages (2 x 64 KB).  The vector-memory path moves ~60 B/clk/CU,
 //     so a K tile's 64 KB occupies it for more than half of the tile's MFMA
 //     time: the fetch of tile t+2 is spread over the middle and last phase of
@@ -23,7 +24,7 @@
 //     loop) instead of being issued in a burst, which would stall the
 //     in-order wave behind a full load queue.
 //   * MXFP8: the 4 E8M0 bytes of a row for the tile's 4 K blocks travel with
-//     the tile (global_load_lds_dword); lane half h shifts its row's word by
+//     the tile (buffer_load_dword ... lds); lane half h shifts its row's word by
 //     8h so that op_sel 0 / 2 pick the bytes of K blocks h / 2+h for the two
 //     64-K MFMA steps (the MFMA operand K order: lane half h holds K
 //     [16h, 16h+16) and [32+16h, 48+16h) of a step; the scale of lanes 0..31
@@ -32,9 +33,11 @@
 //     round-robin over the 8 XCDs; the workgroups of an XCD take turns over a
 //     contiguous range of the tile order, walked in groups of 4 tile-rows x
 //     all tile-columns, so the 32 tiles an XCD runs at once share 4 A panels
-//     and 8 B panels in its L2.  The next tile's first K tiles are fetched
-//     before the current tile's results are written out (through a separate
-//     LDS band), so that fetch overlaps the epilogue.
+//     and 8 B panels in its L2.  The operand stream runs across tile
+//     boundaries: the last two K steps of a tile fetch the next tile's first
+//     two K tiles, and the results are written out through separate LDS bands
+//     without waiting for any fetch, so the next tile starts on operands
+//     that are already in LDS.
 #include <hip/hip_runtime.h>
 
 #include "qsg_device.h"
@@ -71,37 +74,58 @@ struct FastArgs {
 // every 8-row group all 32 of the lower or upper half.
 __device__ __forceinline__ int row_swizzle(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-// Byte offsets (from the operand base, without k0) of the chunks this thread
-// fetches for a ROWS-row tile: instruction i of wave w fills 1 KB block
-// i * 4 + w of the stage.
-template <int ROWS>
-__device__ __forceinline__ void chunk_offsets(uint32_t (&off)[ROWS * CH / 256], int64_t row0, int64_t nrows,
-                                              int64_t ld) {
+
+// global -> LDS loads through buffer resources: lane L's 16 (or 4) bytes go
+// to position L of the LDS block at `lds` (wave-uniform).  The resource of a
+// tile starts at its first row and ends at the matrix's last row, so rows
+// past M / N read as zero (their results are never stored) and the
+// per-thread offsets do not depend on the tile.  The stages are distinct
+// __shared__ objects, so the compiler needs no wait before reading one stage
+// while loads into the other are in flight; the kernel orders the loads with
+// counted vmcnt waits and barriers.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
+}
+
+constexpr int NCHUNK = FBM * CH / 256;  // fetch instructions per wave per operand tile
+static_assert(FBM == FBN, "A and B tiles share the chunk mapping");
+
+// Per-thread byte offsets, within a tile, of the chunks this thread fetches:
+// instruction i of wave w fills 1 KB block i * 4 + w of a stage, lane L its
+// 16-byte position L, i.e. tile row (i*4+w)*8 + L/8 at swizzled chunk L%8.
+__device__ __forceinline__ void chunk_offsets(uint32_t (&off)[NCHUNK], int64_t ld) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < ROWS * CH / 256; ++i) {
-    const int blk = i * 4 + wave;
-    const int slot = blk * 64 + lane;
+  for (int i = 0; i < NCHUNK; ++i) {
+    const int slot = (i * 4 + wave) * 64 + lane;
     const int row = slot / CH, pc = slot % CH;
-    const int c = pc ^ row_swizzle(row);
-    int64_t gr = row0 + row;
-    if (gr > nrows - 1) gr = nrows - 1;
-    off[i] = (uint32_t)(gr * ld + c * 16);
+    off[i] = (uint32_t)(row * ld + ((pc ^ row_swizzle(row)) * 16));
   }
 }
 
-template <int ROWS>
-__device__ __forceinline__ void issue_tile(const uint8_t* base, const uint32_t (&off)[ROWS * CH / 256],
-                                           int64_t k0, uint8_t* lds) {
-  const int wave = threadIdx.x >> 6;
-  const uint8_t* p = base + k0;
-#pragma unroll
-  for (int i = 0; i < ROWS * CH / 256; ++i) {
-    const int blk = i * 4 + wave;
-    __builtin_amdgcn_global_load_lds((const void*)(p + off[i]), (lds_ptr_t)(lds + blk * 1024), 16, 0, 0);
-  }
+// The buffers of one 256 x 256 tile (A rows, B rows, and for MXFP8 their
+// E8M0 rows).
+struct TileRes {
+  __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
+};
+
+// Materializes a step's fetch resources where it starts (the selection is
+// then scheduled with the first phase's MFMAs, not between the fetches).
+template <bool MX>
+__device__ __forceinline__ void pin_res(TileRes& t, uint32_t& k) {
+  if constexpr (MX)
+    asm volatile("" : "+s"(t.ra), "+s"(t.rb), "+s"(t.rsa), "+s"(t.rsb), "+s"(k));
+  else
+    asm volatile("" : "+s"(t.ra), "+s"(t.rb), "+s"(k));
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int64_t row0, int64_t nrows, int64_t ld) {
+  const uint8_t* p = reinterpret_cast<const uint8_t*>(base) + row0 * ld;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, 0, (int)((nrows - row0) * ld), 0x00020000);
+}
 // A 32-row fragment: `row_off` is the byte offset of this lane's row of the
 // first 32-row slice, `c_lo` / `c_hi` the swizzled byte offsets of its two
 // 16-byte chunks (the swizzle only depends on row & 7, which is the same for
@@ -144,36 +168,30 @@ __device__ __forceinline__ uint32_t* stage_sa() { return S ? lds_sa1 : lds_sa0; 
 template <int S>
 __device__ __forceinline__ uint32_t* stage_sb() { return S ? lds_sb1 : lds_sb0; }
 
-template <int S>
-__device__ __forceinline__ void issue_stage(const FastArgs& g, const uint32_t (&offa)[FBM * CH / 256],
-                                            const uint32_t (&offb)[FBN * CH / 256], const uint8_t* sa_row,
-                                            const uint8_t* sb_row, bool mx, int64_t kt) {
-  issue_tile<FBM>(g.a, offa, kt * FBK, stage_a<S>());
-  issue_tile<FBN>(g.b, offb, kt * FBK, stage_b<S>());
-  if (mx) {
-    const int wave = threadIdx.x >> 6;
-    __builtin_amdgcn_global_load_lds((const void*)(sa_row + kt * 4), (lds_ptr_t)(stage_sa<S>() + wave * 64), 4, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(sb_row + kt * 4), (lds_ptr_t)(stage_sb<S>() + wave * 64), 4, 0, 0);
-  }
-}
-
-// Half of a stage's fetch: part 0 = the A tile (+ MX scale words), part 1 = the B tile.
-template <int S, int PART>
-__device__ __forceinline__ void issue_part(const FastArgs& g, const uint32_t (&offa)[FBM * CH / 256],
-                                           const uint32_t (&offb)[FBN * CH / 256], const uint8_t* sa_row,
-                                           const uint8_t* sb_row, bool mx, int64_t kt) {
+// Fetch of K tile kt of a tile into stage S: part 0 = the A tile (+ MX
+// scale words), part 1 = the B tile; `wl` is this wave's 1 KB block offset.
+template <int S, int PART, bool MX>
+__device__ __forceinline__ void issue_part(const TileRes& t, const uint32_t (&voa)[NCHUNK],
+                                           const uint32_t (&vob)[NCHUNK], uint32_t vos, uint32_t wl, uint32_t kt) {
   if constexpr (PART == 0) {
-    issue_tile<FBM>(g.a, offa, kt * FBK, stage_a<S>());
-    if (mx) {
-      const int wave = threadIdx.x >> 6;
-      __builtin_amdgcn_global_load_lds((const void*)(sa_row + kt * 4), (lds_ptr_t)(stage_sa<S>() + wave * 64), 4, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(sb_row + kt * 4), (lds_ptr_t)(stage_sb<S>() + wave * 64), 4, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NCHUNK; ++i) dma16(t.ra, voa[i], kt * FBK, stage_a<S>() + i * 4096 + wl);
+    if constexpr (MX) {
+      dma4(t.rsa, vos, kt * 4, stage_sa<S>() + wl / 16);
+      dma4(t.rsb, vos, kt * 4, stage_sb<S>() + wl / 16);
     }
   } else {
-    issue_tile<FBN>(g.b, offb, kt * FBK, stage_b<S>());
+#pragma unroll
+    for (int i = 0; i < NCHUNK; ++i) dma16(t.rb, vob[i], kt * FBK, stage_b<S>() + i * 4096 + wl);
   }
 }
 
+template <int S, bool MX>
+__device__ __forceinline__ void issue_stage(const TileRes& t, const uint32_t (&voa)[NCHUNK],
+                                            const uint32_t (&vob)[NCHUNK], uint32_t vos, uint32_t wl, uint32_t kt) {
+  issue_part<S, 0, MX>(t, voa, vob, vos, wl, kt);
+  issue_part<S, 1, MX>(t, voa, vob, vos, wl, kt);
+}
 // s_waitcnt vmcnt(N) lgkmcnt(0)
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {
@@ -219,6 +237,30 @@ __device__ __forceinline__ void mfma_range(v16f (&acc)[TMW][TNW], const Frags& f
   }
 }
 
+// An accumulator element copied to a VGPR (keeps the accumulators in AGPRs
+// for the register allocator).
+__device__ __forceinline__ float acc_read(float a) {
+  float v;
+  asm("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) uint8_t gbyte;
+
+// Band accesses as inline assembly: the compiler cannot tell the band from
+// the operand stages that global->LDS loads are filling and would wait for
+// all of them before the first band access.  The waits these need are
+// explicit.
+__device__ __forceinline__ void band_write(uint32_t addr, u32x2 v) { asm volatile("ds_write_b64 %0, %1" : : "v"(addr), "v"(v)); }
+__device__ __forceinline__ void band_write(uint32_t addr, u32x4 v) { asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v)); }
+__device__ __forceinline__ u32x4 band_read(uint32_t addr) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+
 // Epilogue staging: per wave a band of 32 rows x 128 bytes of C, with a
 // padded row stride (bf16 136 B, fp32 144 B) that keeps the accumulator
 // writes (8 or 16 bytes for 32 rows at one column) free of bank conflicts.
@@ -230,11 +272,12 @@ __shared__ __attribute__((aligned(256))) uint8_t lds_c[4][32 * EPI_STRIDE_MAX];
 // Tile t of the XCD-aware order: workgroup ids are dispatched round-robin
 // over the 8 XCDs, each XCD owns a contiguous range of the logical tile
 // order, walked in groups of 4 tile-rows x all tile-columns.
-__device__ __forceinline__ void tile_coords(const FastArgs& g, int64_t logical, int64_t& m0, int64_t& n0) {
-  constexpr int64_t GM = 4;
-  const int64_t per_group = GM * g.tiles_n;
-  const int64_t first_m = (logical / per_group) * GM;
-  const int64_t gsize = (g.tiles_m - first_m) < GM ? (g.tiles_m - first_m) : GM;
+__device__ __forceinline__ void tile_coords(const FastArgs& g, uint32_t logical, uint32_t& m0, uint32_t& n0) {
+  constexpr uint32_t GM = 4;
+  const uint32_t tm = (uint32_t)g.tiles_m, tn = (uint32_t)g.tiles_n;
+  const uint32_t per_group = GM * tn;
+  const uint32_t first_m = (logical / per_group) * GM;
+  const uint32_t gsize = (tm - first_m) < GM ? (tm - first_m) : GM;
   m0 = (first_m + (logical % per_group) % gsize) * FBM;
   n0 = ((logical % per_group) / gsize) * FBN;
 }
@@ -242,21 +285,22 @@ __device__ __forceinline__ void tile_coords(const FastArgs& g, int64_t logical, 
 template <bool MX, int FA, int FB, bool OUT_BF16>
 __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
   constexpr int WM = FBM / 2, WN = FBN / 2;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   // Persistent workgroups: the ones on XCD x (ids x, x+8, ...) take turns
   // over XCD x's contiguous range of logical tiles.
-  const int64_t T = g.tiles_m * g.tiles_n;
-  const int64_t G = gridDim.x;
-  const int64_t xcd = blockIdx.x % 8, local = blockIdx.x / 8;
-  const int64_t per = T / 8, rem = T % 8;
-  const int64_t x_begin = xcd * per + (xcd < rem ? xcd : rem);
-  const int64_t x_end = x_begin + per + (xcd < rem ? 1 : 0);
-  const int64_t x_wgs = G / 8 + (xcd < G % 8 ? 1 : 0);
-  int64_t logical = x_begin + local;
+  const uint32_t T = (uint32_t)(g.tiles_m * g.tiles_n);
+  const uint32_t G = gridDim.x;
+  const uint32_t xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+  const uint32_t per = T / 8, rem = T % 8;
+  const uint32_t x_begin = xcd * per + (xcd < rem ? xcd : rem);
+  const uint32_t x_end = x_begin + per + (xcd < rem ? 1 : 0);
+  const uint32_t x_wgs = G / 8 + (xcd < G % 8 ? 1 : 0);
+  uint32_t logical = x_begin + local;
   if (logical >= x_end) return;
-  const int64_t nk = g.K / FBK;  // even (checked by the launcher)
+  const uint32_t nk = (uint32_t)(g.K / FBK);  // even (checked by the launcher)
+  const uint32_t nb = (uint32_t)(g.K / 32);   // MX: E8M0 bytes per row
 
   // fragment addressing: lane half h reads chunks kk*4 + h and kk*4 + 2 + h
   const int a_row_off = (wm * WM + (lane & 31)) * FBK;
@@ -270,57 +314,69 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
   float alpha = 1.0f;
   if constexpr (!MX) alpha = *reinterpret_cast<const float*>(g.sa) * *reinterpret_cast<const float*>(g.sb);
 
-  int64_t m0, n0;
-  tile_coords(g, logical, m0, n0);
-  uint32_t offa[FBM * CH / 256], offb[FBN * CH / 256];
-  const uint8_t* sa_row = nullptr;
-  const uint8_t* sb_row = nullptr;
-  auto tile_setup = [&]() {
-    chunk_offsets<FBM>(offa, m0, g.M, g.lda);
-    chunk_offsets<FBN>(offb, n0, g.N, g.ldb);
+  uint32_t voa[NCHUNK], vob[NCHUNK];
+  chunk_offsets(voa, g.lda);
+  chunk_offsets(vob, g.ldb);
+  const uint32_t vos = (uint32_t)(threadIdx.x * nb);
+  const uint32_t wl = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
+  auto resources = [&](uint32_t tm0, uint32_t tn0) {
+    TileRes t;
+    t.ra = rows_rsrc(g.a, tm0, g.M, g.lda);
+    t.rb = rows_rsrc(g.b, tn0, g.N, g.ldb);
     if constexpr (MX) {
-      const int64_t nb = g.K / 32;
-      int64_t ra = m0 + threadIdx.x, rb = n0 + threadIdx.x;
-      if (ra > g.M - 1) ra = g.M - 1;
-      if (rb > g.N - 1) rb = g.N - 1;
-      sa_row = reinterpret_cast<const uint8_t*>(g.sa) + ra * nb;
-      sb_row = reinterpret_cast<const uint8_t*>(g.sb) + rb * nb;
+      t.rsa = rows_rsrc(g.sa, tm0, g.M, nb);
+      t.rsb = rows_rsrc(g.sb, tn0, g.N, nb);
     }
+    return t;
   };
+
+  uint32_t m0, n0;
+  tile_coords(g, logical, m0, n0);
+  TileRes cur = resources(m0, n0);
   constexpr int P1 = 9, P2 = 7;
-  constexpr int NA = FBM * CH / 256 + (MX ? 2 : 0);  // fetches in a part-0 issue
-  constexpr int NS = 2 * (FBM * CH / 256) + (MX ? 2 : 0);  // fetches of a whole stage
-  constexpr int NSTORE = (OUT_BF16 ? 32 : 64);  // epilogue stores per wave
-  tile_setup();
-  issue_stage<0>(g, offa, offb, sa_row, sb_row, MX, 0);
-  issue_stage<1>(g, offa, offb, sa_row, sb_row, MX, 1);
+  constexpr int NA = NCHUNK + (MX ? 2 : 0);      // fetches in a part-0 issue
+  constexpr int NS = 2 * NCHUNK + (MX ? 2 : 0);  // fetches of a whole stage
+  issue_stage<0, MX>(cur, voa, vob, vos, wl, 0);
+  issue_stage<1, MX>(cur, voa, vob, vos, wl, 1);
   wait_vm_lgkm0<NS>();  // stage 0 landed
+  lds_barrier();
 
   v16f acc[TMW][TNW];
   Frags f0, f1;
+  load_frags<0, MX>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);
   while (true) {
+    // The next tile's resources: the fetches of the last two K steps go to
+    // its first two K tiles (or repeat this tile's, past the last tile), so
+    // the operand stream runs on across the tile boundary.
+    const int64_t cm0 = m0, cn0 = n0;
+    const uint32_t nlogical = logical + x_wgs;
+    const bool more = nlogical < x_end;
+    uint32_t nm0 = m0, nn0 = n0;
+    if (more) tile_coords(g, nlogical, nm0, nn0);
+    const TileRes nxt_t = resources(nm0, nn0);
 #pragma unroll
     for (int i = 0; i < TMW; ++i)
 #pragma unroll
       for (int j = 0; j < TNW; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-    lds_barrier();  // stage 0 is complete for every wave
-    load_frags<0, MX>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);
 
   // One K tile KT in stage S (f0 holds its first 64-K fragments), in three
   // phases around two barriers:
   //   1. MFMAs 0..P1-1 of f0; the second-step fragments f1 are read from S.
   //   2. barrier (every wave is done reading S); MFMAs P1..15 of f0 and
-  //      0..P2-1 of f1; the A half of tile KT+2 is fetched into S.
-  //   3. wait for this wave's fetches of tile KT+1, barrier (tile KT+1 is
-  //      complete in S^1); MFMAs P2..15 of f1; the first-step fragments of
-  //      KT+1 are read from S^1 and the B half of KT+2 is fetched into S.
-  // The fetch of a tile is spread over phases 2 and 3 and has until phase 3
-  // of the next step to land.  Past the last tile the fetch repeats the last
-  // tile and is unused, which keeps the body branch-free.
+  //      0..P2-1 of f1; the A half of the K tile two ahead is fetched into S.
+  //   3. wait for this wave's fetches of the next K tile, barrier (it is
+  //      complete in S^1); MFMAs P2..15 of f1; the next K tile's first-step
+  //      fragments are read from S^1 and the B half of the K tile two ahead
+  //      is fetched into S.
+  // Two ahead of the last K tiles are the next tile's first two.
 #define QSG_FAST_STEP(S, KT)                                                                   \
   {                                                                                            \
+    const bool own = (KT) + 2 < nk;                                                            \
+    TileRes RES = own ? cur : nxt_t;                                                           \
+    uint32_t FK = own ? (KT) + 2 : (KT) + 2 - nk;                                              \
+    pin_res<MX>(RES, FK);                                                                          \
     load_frags<S, MX>(f1, 1, a_row_off, b_row_off, c10, c11, a_srow, b_srow, sh1);             \
     mfma_range<MX, FA, FB, 0, P1>(acc, f0);                                                    \
     _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                            \
@@ -331,49 +387,43 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     __builtin_amdgcn_sched_barrier(0);                                                         \
     wait_vm_lgkm0<63>();                                                                       \
     lds_barrier();                                                                             \
-    const int64_t nxt = (KT) + 2 < nk ? (KT) + 2 : nk - 1;                                     \
-    issue_part<S, 0>(g, offa, offb, sa_row, sb_row, MX, nxt);                                  \
+    issue_part<S, 0, MX>(RES, voa, vob, vos, wl, FK);                                          \
     mfma_range<MX, FA, FB, P1, 16>(acc, f0);                                                   \
     mfma_range<MX, FA, FB, 0, P2>(acc, f1);                                                    \
     _Pragma("unroll") for (int q = 0; q < NA; ++q) {                                           \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);                                       \
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);                                       \
+      __builtin_amdgcn_sched_group_barrier(0x001, 3, 1);                                       \
     }                                                                                          \
     __builtin_amdgcn_sched_group_barrier(0x008, 16 - P1 + P2 - NA, 1);                         \
     __builtin_amdgcn_sched_barrier(0);                                                         \
     wait_vm_lgkm0<NA>();                                                                       \
     lds_barrier();                                                                             \
     load_frags<S ^ 1, MX>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);         \
-    issue_part<S, 1>(g, offa, offb, sa_row, sb_row, MX, nxt);                                  \
+    issue_part<S, 1, MX>(RES, voa, vob, vos, wl, FK);                                          \
     mfma_range<MX, FA, FB, P2, 16>(acc, f1);                                                   \
     _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                            \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);                                       \
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);                                       \
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 2);                                       \
+      __builtin_amdgcn_sched_group_barrier(0x001, 3, 2);                                       \
     }                                                                                          \
     __builtin_amdgcn_sched_group_barrier(0x008, 16 - P2 - 8, 2);                               \
     __builtin_amdgcn_sched_barrier(0);                                                         \
   }
 
-    for (int64_t kt = 0; kt < nk; kt += 2) {
+    // nk >= 2: a do-while leaves the compiler no path that skips the loop
+    // (merging the zeroed accumulators of such a path with the loop's costs
+    // accumulator copies and spills in the epilogue)
+    uint32_t kt = 0;
+    do {
       QSG_FAST_STEP(0, kt)
       QSG_FAST_STEP(1, kt + 1)
-    }
+      kt += 2;
+    } while (kt < nk);
 #undef QSG_FAST_STEP
-    // every wave is done with the operand stages
-    __builtin_amdgcn_s_waitcnt(0);
-    lds_barrier();
-
-    // next tile: fetch its first two K tiles now, so that they land while
-    // this tile's results are written out
-    const int64_t cm0 = m0, cn0 = n0;
-    logical += x_wgs;
-    const bool more = logical < x_end;
-    if (more) {
-      tile_coords(g, logical, m0, n0);
-      tile_setup();
-      issue_stage<0>(g, offa, offb, sa_row, sb_row, MX, 0);
-    }
+    // The next tile's first K tile is in stage 0, its second on the way to
+    // stage 1.  The epilogue uses its own LDS bands and waits for no fetch.
+    // (The last step's reads of f0 are repeated after it, so that the
+    // fragments are not held through the epilogue.)
 
     // ---- epilogue: scale, convert, stage through LDS, coalesced stores ----
     // Each wave owns a 128 x 128 block of C, written as bands of 32 rows x
@@ -383,73 +433,89 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     constexpr int STRIDE = OUT_BF16 ? 136 : 144;
     constexpr int BCOLS = 128 / ESZ;  // columns per band
     constexpr int JPB = BCOLS / 32;   // accumulator column tiles per band
-    uint8_t* band = lds_c[wave];
-    const int64_t bm0 = cm0 + wm * WM, bn0 = cn0 + wn * WN;
-    const int sl = lane % 8, sr = lane / 8;
+    const uint32_t band = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_c[wave];
+    // tile coordinates made opaque here, so that no address below is
+    // computed ahead of the K loop and kept live across it
+    uint32_t em0 = (uint32_t)cm0, en0 = (uint32_t)cn0;
+    int64_t ldc = g.ldc;
+    gbyte* cbase = (gbyte*)g.c;
+    asm volatile("" : "+s"(em0), "+s"(en0), "+s"(ldc), "+s"(cbase));
+    const int64_t bm0 = (int64_t)em0 + wm * WM, bn0 = (int64_t)en0 + wn * WN;
+    int elane = lane;
+    asm volatile("" : "+v"(elane));
+    const int sl = elane % 8, sr = elane / 8;
+    const bool interior = g.vec_c && bm0 - wm * WM + FBM <= g.M && bn0 - wn * WN + FBN <= g.N;
+    // this lane's byte offset (band row sr, segment sl) from a band's first element
+    const uint32_t lo = ((uint32_t)sr * (uint32_t)ldc + (uint32_t)(sl * (16 / ESZ))) * ESZ;
+    gbyte* const cw = cbase + (bm0 * ldc + bn0) * ESZ;  // wave-uniform
+    const uint32_t wr_lane = band + (uint32_t)((elane & 31) * STRIDE + (elane >> 5) * 4 * ESZ);
+    const uint32_t rd_lane = band + (uint32_t)(sr * STRIDE + sl * 16);
 #pragma unroll
     for (int i = 0; i < TMW; ++i) {
 #pragma unroll
       for (int jb = 0; jb < TNW / JPB; ++jb) {
-        const int r = lane & 31;
 #pragma unroll
         for (int jj = 0; jj < JPB; ++jj) {
           const int j = jb * JPB + jj;
 #pragma unroll
           for (int grp = 0; grp < 4; ++grp) {
-            const int col = jj * 32 + grp * 8 + (lane >> 5) * 4;
-            const float v0 = acc[i][j][grp * 4 + 0] * alpha, v1 = acc[i][j][grp * 4 + 1] * alpha;
-            const float v2 = acc[i][j][grp * 4 + 2] * alpha, v3 = acc[i][j][grp * 4 + 3] * alpha;
-            uint8_t* dst = band + r * STRIDE + col * ESZ;
+            const uint32_t dst = wr_lane + (uint32_t)((jj * 32 + grp * 8) * ESZ);
+            const float v0 = acc_read(acc[i][j][grp * 4 + 0]) * alpha, v1 = acc_read(acc[i][j][grp * 4 + 1]) * alpha;
+            const float v2 = acc_read(acc[i][j][grp * 4 + 2]) * alpha, v3 = acc_read(acc[i][j][grp * 4 + 3]) * alpha;
             if constexpr (OUT_BF16) {
-              *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+              const u32x2 w = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+              band_write(dst, w);
             } else {
-              *reinterpret_cast<uint4*>(dst) =
-                  make_uint4(__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2), __float_as_uint(v3));
+              const u32x4 w = {__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2), __float_as_uint(v3)};
+              band_write(dst, w);
             }
           }
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's band writes are done
         __builtin_amdgcn_wave_barrier();
+        // the four 16-byte reads, one wait, then the stores
+        u32x4 pv[4];
 #pragma unroll
-        for (int rr = 0; rr < 32; rr += 8) {
-          const int rw = rr + sr;
-          const int64_t m = bm0 + i * 32 + rw;
-          const int64_t n = bn0 + jb * BCOLS + sl * (16 / ESZ);
-          const uint4 v = *reinterpret_cast<const uint4*>(band + rw * STRIDE + sl * 16);
-          if (m < g.M) {
-            uint8_t* cp = reinterpret_cast<uint8_t*>(g.c) + (m * g.ldc + n) * ESZ;
-            if (g.vec_c && n + 16 / ESZ <= g.N) {
-              *reinterpret_cast<uint4*>(cp) = v;
-            } else {
-              const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        for (int q = 0; q < 4; ++q) pv[q] = band_read(rd_lane + (uint32_t)(q * 8 * STRIDE));
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(pv[0]), "+v"(pv[1]), "+v"(pv[2]), "+v"(pv[3]));
 #pragma unroll
-              for (int e = 0; e < 16 / ESZ; ++e) {
-                if (n + e < g.N) {
-                  if constexpr (OUT_BF16)
-                    reinterpret_cast<uint16_t*>(cp)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-                  else
-                    reinterpret_cast<uint32_t*>(cp)[e] = w[e];
+        for (int q = 0; q < 4; ++q) {
+          gbyte* const cp = cw + ((int64_t)(i * 32 + q * 8) * ldc + jb * BCOLS) * ESZ + lo;
+          if (interior) {
+            *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(cp) = pv[q];
+          } else {
+            const int m = (int)bm0 + i * 32 + q * 8 + sr;
+            const int n = (int)bn0 + jb * BCOLS + sl * (16 / ESZ);
+            if (m < g.M) {
+              if (g.vec_c && n + 16 / ESZ <= g.N) {
+                *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(cp) = pv[q];
+              } else {
+#pragma unroll
+                for (int e = 0; e < 16 / ESZ; ++e) {
+                  if (n + e < g.N) {
+                    if constexpr (OUT_BF16)
+                      reinterpret_cast<__attribute__((address_space(1))) uint16_t*>(cp)[e] =
+                          (uint16_t)(pv[q][e >> 1] >> (16 * (e & 1)));
+                    else
+                      reinterpret_cast<__attribute__((address_space(1))) uint32_t*>(cp)[e] = pv[q][e];
+                  }
                 }
               }
             }
           }
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // band reads done before the next band overwrites it
-        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_wave_barrier();  // (the band reads completed at the wait above)
       }
     }
-    if (!more) break;
-    // The stores are in flight; stage 1 is fetched behind them.  For a tile
-    // inside the matrix every lane stores every segment, so exactly NSTORE
-    // store instructions are younger than stage 0 and it alone is waited
-    // for (the stores must land by the first wait for stage 1, in the next
-    // tile's first step).  An edge tile skips or splits stores, so there
-    // the wait also covers its stores.
-    issue_stage<1>(g, offa, offb, sa_row, sb_row, MX, 1);
-    if (g.vec_c && cm0 + FBM <= g.M && cn0 + FBN <= g.N)
-      wait_vm_lgkm0<(NSTORE + NS < 63 ? NSTORE + NS : 63)>();
-    else
-      wait_vm_lgkm0<NS>();
+    if (!more) {
+      wait_vm_lgkm0<0>();  // the repeated fetches of the last step land before the workgroup ends
+      break;
+    }
+    logical = nlogical;
+    m0 = nm0;
+    n0 = nn0;
+    cur = nxt_t;
+    load_frags<0, MX>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);
   }
 }
 

@@ -35,7 +35,7 @@
 //     all tile-columns, so the 32 tiles an XCD runs at once share 4 A panels
 //     and 8 B panels in its L2.  The operand stream runs across tile
 //     boundaries: the last two K steps of a tile fetch the next tile's first
-//     two K tiles, and the results are written out through separate LDS bands
+//     two K tiles, and the results are stored straight from registers
 //     without waiting for any fetch, so the next tile starts on operands
 //     that are already in LDS.
 #include <hip/hip_runtime.h>
@@ -245,29 +245,8 @@ __device__ __forceinline__ float acc_read(float a) {
   return v;
 }
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) uint8_t gbyte;
-
-// Band accesses as inline assembly: the compiler cannot tell the band from
-// the operand stages that global->LDS loads are filling and would wait for
-// all of them before the first band access.  The waits these need are
-// explicit.
-__device__ __forceinline__ void band_write(uint32_t addr, u32x2 v) { asm volatile("ds_write_b64 %0, %1" : : "v"(addr), "v"(v)); }
-__device__ __forceinline__ void band_write(uint32_t addr, u32x4 v) { asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v)); }
-__device__ __forceinline__ u32x4 band_read(uint32_t addr) {
-  u32x4 v;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
-  return v;
-}
-
-// Epilogue staging: per wave a band of 32 rows x 128 bytes of C, with a
-// padded row stride (bf16 136 B, fp32 144 B) that keeps the accumulator
-// writes (8 or 16 bytes for 32 rows at one column) free of bank conflicts.
-// It lives outside the operand stages, so the next tile's operands can be
-// fetched while the band is written out.
-constexpr int EPI_STRIDE_MAX = 144;
-__shared__ __attribute__((aligned(256))) uint8_t lds_c[4][32 * EPI_STRIDE_MAX];
 
 // Tile t of the XCD-aware order: workgroup ids are dispatched round-robin
 // over the 8 XCDs, each XCD owns a contiguous range of the logical tile
@@ -421,19 +400,17 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     } while (kt < nk);
 #undef QSG_FAST_STEP
     // The next tile's first K tile is in stage 0, its second on the way to
-    // stage 1.  The epilogue uses its own LDS bands and waits for no fetch.
+    // stage 1.  The epilogue stores from registers and waits for no fetch.
     // (The last step's reads of f0 are repeated after it, so that the
     // fragments are not held through the epilogue.)
 
-    // ---- epilogue: scale, convert, stage through LDS, coalesced stores ----
-    // Each wave owns a 128 x 128 block of C, written as bands of 32 rows x
-    // 128 bytes: the accumulators go to the wave's LDS band, then every store
-    // instruction writes 8 whole 128-byte row segments.
+    // ---- epilogue: scale, convert, store straight from registers ----
+    // In a 32 x 32 accumulator tile, lane l holds row l % 32 and, for group
+    // g = 0..3, columns 8g + 4(l / 32) + 0..3.  For bf16 a lane swap between
+    // the halves (v_permlane32_swap) of groups 2p and 2p + 1 gives every lane
+    // 8 consecutive columns (16 bytes): lanes l and l + 32 then write one
+    // 32-byte piece of row l % 32.  fp32 groups are 16 bytes already.
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
-    constexpr int STRIDE = OUT_BF16 ? 136 : 144;
-    constexpr int BCOLS = 128 / ESZ;  // columns per band
-    constexpr int JPB = BCOLS / 32;   // accumulator column tiles per band
-    const uint32_t band = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_c[wave];
     // tile coordinates made opaque here, so that no address below is
     // computed ahead of the K loop and kept live across it
     uint32_t em0 = (uint32_t)cm0, en0 = (uint32_t)cn0;
@@ -443,68 +420,69 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     const int64_t bm0 = (int64_t)em0 + wm * WM, bn0 = (int64_t)en0 + wn * WN;
     int elane = lane;
     asm volatile("" : "+v"(elane));
-    const int sl = elane % 8, sr = elane / 8;
+    const int er = elane & 31, eh = elane >> 5;
     const bool interior = g.vec_c && bm0 - wm * WM + FBM <= g.M && bn0 - wn * WN + FBN <= g.N;
-    // this lane's byte offset (band row sr, segment sl) from a band's first element
-    const uint32_t lo = ((uint32_t)sr * (uint32_t)ldc + (uint32_t)(sl * (16 / ESZ))) * ESZ;
     gbyte* const cw = cbase + (bm0 * ldc + bn0) * ESZ;  // wave-uniform
-    const uint32_t wr_lane = band + (uint32_t)((elane & 31) * STRIDE + (elane >> 5) * 4 * ESZ);
-    const uint32_t rd_lane = band + (uint32_t)(sr * STRIDE + sl * 16);
+    const uint32_t lrow = (uint32_t)er * (uint32_t)ldc * ESZ;  // this lane's row offset in bytes
 #pragma unroll
     for (int i = 0; i < TMW; ++i) {
 #pragma unroll
-      for (int jb = 0; jb < TNW / JPB; ++jb) {
+      for (int j = 0; j < TNW; ++j) {
+        u32x4 piece[4];  // bf16: pieces 0, 1 used; fp32: 4 pieces
+        int pcol[4];     // column of each piece within the 128-column block
+        if constexpr (OUT_BF16) {
+          uint32_t pk[4][2];
 #pragma unroll
-        for (int jj = 0; jj < JPB; ++jj) {
-          const int j = jb * JPB + jj;
+          for (int gq = 0; gq < 4; ++gq) {
+            const float v0 = acc_read(acc[i][j][gq * 4 + 0]) * alpha, v1 = acc_read(acc[i][j][gq * 4 + 1]) * alpha;
+            const float v2 = acc_read(acc[i][j][gq * 4 + 2]) * alpha, v3 = acc_read(acc[i][j][gq * 4 + 3]) * alpha;
+            pk[gq][0] = pack_bf16x2(v0, v1);
+            pk[gq][1] = pack_bf16x2(v2, v3);
+          }
 #pragma unroll
-          for (int grp = 0; grp < 4; ++grp) {
-            const uint32_t dst = wr_lane + (uint32_t)((jj * 32 + grp * 8) * ESZ);
-            const float v0 = acc_read(acc[i][j][grp * 4 + 0]) * alpha, v1 = acc_read(acc[i][j][grp * 4 + 1]) * alpha;
-            const float v2 = acc_read(acc[i][j][grp * 4 + 2]) * alpha, v3 = acc_read(acc[i][j][grp * 4 + 3]) * alpha;
-            if constexpr (OUT_BF16) {
-              const u32x2 w = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-              band_write(dst, w);
-            } else {
-              const u32x4 w = {__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2), __float_as_uint(v3)};
-              band_write(dst, w);
-            }
+          for (int p = 0; p < 2; ++p) {
+            const auto s0 = __builtin_amdgcn_permlane32_swap(pk[2 * p][0], pk[2 * p + 1][0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(pk[2 * p][1], pk[2 * p + 1][1], false, false);
+            piece[p] = u32x4{s0[0], s1[0], s0[1], s1[1]};
+            pcol[p] = j * 32 + 16 * p + 8 * eh;
+          }
+        } else {
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const float v0 = acc_read(acc[i][j][gq * 4 + 0]) * alpha, v1 = acc_read(acc[i][j][gq * 4 + 1]) * alpha;
+            const float v2 = acc_read(acc[i][j][gq * 4 + 2]) * alpha, v3 = acc_read(acc[i][j][gq * 4 + 3]) * alpha;
+            piece[gq] = u32x4{__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2), __float_as_uint(v3)};
+            pcol[gq] = j * 32 + 8 * gq + 4 * eh;
           }
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's band writes are done
-        __builtin_amdgcn_wave_barrier();
-        // the four 16-byte reads, one wait, then the stores
-        u32x4 pv[4];
+        constexpr int NP = OUT_BF16 ? 2 : 4;
+        constexpr int PE = 16 / ESZ;  // elements per piece
 #pragma unroll
-        for (int q = 0; q < 4; ++q) pv[q] = band_read(rd_lane + (uint32_t)(q * 8 * STRIDE));
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(pv[0]), "+v"(pv[1]), "+v"(pv[2]), "+v"(pv[3]));
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          gbyte* const cp = cw + ((int64_t)(i * 32 + q * 8) * ldc + jb * BCOLS) * ESZ + lo;
+        for (int p = 0; p < NP; ++p) {
+          gbyte* const cp = cw + (int64_t)(i * 32) * ldc * ESZ + lrow + pcol[p] * ESZ;
           if (interior) {
-            *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(cp) = pv[q];
+            *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(cp) = piece[p];
           } else {
-            const int m = (int)bm0 + i * 32 + q * 8 + sr;
-            const int n = (int)bn0 + jb * BCOLS + sl * (16 / ESZ);
+            const int m = (int)bm0 + i * 32 + er;
+            const int n = (int)bn0 + pcol[p];
             if (m < g.M) {
-              if (g.vec_c && n + 16 / ESZ <= g.N) {
-                *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(cp) = pv[q];
+              if (g.vec_c && n + PE <= g.N) {
+                *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(cp) = piece[p];
               } else {
 #pragma unroll
-                for (int e = 0; e < 16 / ESZ; ++e) {
+                for (int e = 0; e < PE; ++e) {
                   if (n + e < g.N) {
                     if constexpr (OUT_BF16)
                       reinterpret_cast<__attribute__((address_space(1))) uint16_t*>(cp)[e] =
-                          (uint16_t)(pv[q][e >> 1] >> (16 * (e & 1)));
+                          (uint16_t)(piece[p][e >> 1] >> (16 * (e & 1)));
                     else
-                      reinterpret_cast<__attribute__((address_space(1))) uint32_t*>(cp)[e] = pv[q][e];
+                      reinterpret_cast<__attribute__((address_space(1))) uint32_t*>(cp)[e] = piece[p][e];
                   }
                 }
               }
             }
           }
         }
-        __builtin_amdgcn_wave_barrier();  // (the band reads completed at the wait above)
       }
     }
     if (!more) {

@@ -38,6 +38,9 @@
 //     two K tiles, and the results are stored straight from registers
 //     without waiting for any fetch, so the next tile starts on operands
 //     that are already in LDS.
+//   * A last round of tiles that would leave at least half the CUs idle runs
+//     as a second launch of 256 x 128 tiles (each wave 128 x 64), twice as
+//     many work items of half the size.
 #include <hip/hip_runtime.h>
 
 #include "qsg_device.h"
@@ -140,11 +143,14 @@ __device__ __forceinline__ v8i ffrag(const uint8_t* lds, int row_off, int slice,
   return r;
 }
 
-constexpr int TMW = FBM / 2 / 32, TNW = FBN / 2 / 32;  // MFMA tiles per wave
+// MFMA tiles per wave: TMW rows; TN columns (4: 256 x 256 workgroup tile,
+// 2: 256 x 128, for the last partial round of tiles)
+constexpr int TMW = FBM / 2 / 32;
 
+template <int TN>
 struct Frags {
-  v8i a[TMW], b[TNW];
-  int sa[TMW], sb[TNW];  // MX: E8M0 words (byte 0: first 64-K step, byte 2: second)
+  v8i a[TMW], b[TN];
+  int sa[TMW], sb[TN];  // MX: E8M0 words (byte 0: first 64-K step, byte 2: second)
 };
 
 // The operand tiles of the two LDS stages are distinct __shared__ objects so
@@ -170,7 +176,7 @@ __device__ __forceinline__ uint32_t* stage_sb() { return S ? lds_sb1 : lds_sb0; 
 
 // Fetch of K tile kt of a tile into stage S: part 0 = the A tile (+ MX
 // scale words), part 1 = the B tile; `wl` is this wave's 1 KB block offset.
-template <int S, int PART, bool MX>
+template <int S, int PART, bool MX, int TN>
 __device__ __forceinline__ void issue_part(const TileRes& t, const uint32_t (&voa)[NCHUNK],
                                            const uint32_t (&vob)[NCHUNK], uint32_t vos, uint32_t wl, uint32_t kt) {
   if constexpr (PART == 0) {
@@ -182,15 +188,15 @@ __device__ __forceinline__ void issue_part(const TileRes& t, const uint32_t (&vo
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < NCHUNK; ++i) dma16(t.rb, vob[i], kt * FBK, stage_b<S>() + i * 4096 + wl);
+    for (int i = 0; i < NCHUNK * TN / 4; ++i) dma16(t.rb, vob[i], kt * FBK, stage_b<S>() + i * 4096 + wl);
   }
 }
 
-template <int S, bool MX>
+template <int S, bool MX, int TN>
 __device__ __forceinline__ void issue_stage(const TileRes& t, const uint32_t (&voa)[NCHUNK],
                                             const uint32_t (&vob)[NCHUNK], uint32_t vos, uint32_t wl, uint32_t kt) {
-  issue_part<S, 0, MX>(t, voa, vob, vos, wl, kt);
-  issue_part<S, 1, MX>(t, voa, vob, vos, wl, kt);
+  issue_part<S, 0, MX, TN>(t, voa, vob, vos, wl, kt);
+  issue_part<S, 1, MX, TN>(t, voa, vob, vos, wl, kt);
 }
 // s_waitcnt vmcnt(N) lgkmcnt(0)
 template <int N>
@@ -208,28 +214,28 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 
-template <int S, bool MX>
-__device__ __forceinline__ void load_frags(Frags& f, int kk, int a_row_off, int b_row_off, int c_lo, int c_hi,
+template <int S, bool MX, int TN>
+__device__ __forceinline__ void load_frags(Frags<TN>& f, int kk, int a_row_off, int b_row_off, int c_lo, int c_hi,
                                            int a_srow, int b_srow, int sh) {
 #pragma unroll
   for (int i = 0; i < TMW; ++i) f.a[i] = ffrag(stage_a<S>(), a_row_off, i, c_lo, c_hi);
 #pragma unroll
-  for (int j = 0; j < TNW; ++j) f.b[j] = ffrag(stage_b<S>(), b_row_off, j, c_lo, c_hi);
+  for (int j = 0; j < TN; ++j) f.b[j] = ffrag(stage_b<S>(), b_row_off, j, c_lo, c_hi);
   if constexpr (MX) {
 #pragma unroll
     for (int i = 0; i < TMW; ++i) f.sa[i] = (int)(stage_sa<S>()[a_srow + i * 32] >> sh);
 #pragma unroll
-    for (int j = 0; j < TNW; ++j) f.sb[j] = (int)(stage_sb<S>()[b_srow + j * 32] >> sh);
+    for (int j = 0; j < TN; ++j) f.sb[j] = (int)(stage_sb<S>()[b_srow + j * 32] >> sh);
   }
 }
 
 // MFMAs LO..HI-1 of one 64-K step, MFMA q updating accumulator tile
-// (q / TNW, q % TNW).
-template <bool MX, int FA, int FB, int LO, int HI>
-__device__ __forceinline__ void mfma_range(v16f (&acc)[TMW][TNW], const Frags& f) {
+// (q / TN, q % TN).
+template <bool MX, int FA, int FB, int LO, int HI, int TN>
+__device__ __forceinline__ void mfma_range(v16f (&acc)[TMW][TN], const Frags<TN>& f) {
 #pragma unroll
   for (int q = LO; q < HI; ++q) {
-    const int i = q / TNW, j = q % TNW;
+    const int i = q / TN, j = q % TN;
     if constexpr (MX)
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, 0, f.sb[j], 0, f.sa[i]);
     else
@@ -251,6 +257,7 @@ typedef __attribute__((address_space(1))) uint8_t gbyte;
 // Tile t of the XCD-aware order: workgroup ids are dispatched round-robin
 // over the 8 XCDs, each XCD owns a contiguous range of the logical tile
 // order, walked in groups of 4 tile-rows x all tile-columns.
+template <int TN>
 __device__ __forceinline__ void tile_coords(const FastArgs& g, uint32_t logical, uint32_t& m0, uint32_t& n0) {
   constexpr uint32_t GM = 4;
   const uint32_t tm = (uint32_t)g.tiles_m, tn = (uint32_t)g.tiles_n;
@@ -258,12 +265,13 @@ __device__ __forceinline__ void tile_coords(const FastArgs& g, uint32_t logical,
   const uint32_t first_m = (logical / per_group) * GM;
   const uint32_t gsize = (tm - first_m) < GM ? (tm - first_m) : GM;
   m0 = (first_m + (logical % per_group) % gsize) * FBM;
-  n0 = ((logical % per_group) / gsize) * FBN;
+  n0 = ((logical % per_group) / gsize) * (TN * 64);
 }
 
-template <bool MX, int FA, int FB, bool OUT_BF16>
+template <bool MX, int FA, int FB, bool OUT_BF16, int TN>
 __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
-  constexpr int WM = FBM / 2, WN = FBN / 2;
+  constexpr int WM = FBM / 2, WN = TN * 32, TBN = TN * 64;
+  constexpr int NQ = TMW * TN;  // MFMAs per 64-K step
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
@@ -310,19 +318,19 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
   };
 
   uint32_t m0, n0;
-  tile_coords(g, logical, m0, n0);
+  tile_coords<TN>(g, logical, m0, n0);
   TileRes cur = resources(m0, n0);
-  constexpr int P1 = 9, P2 = 7;
-  constexpr int NA = NCHUNK + (MX ? 2 : 0);      // fetches in a part-0 issue
-  constexpr int NS = 2 * NCHUNK + (MX ? 2 : 0);  // fetches of a whole stage
-  issue_stage<0, MX>(cur, voa, vob, vos, wl, 0);
-  issue_stage<1, MX>(cur, voa, vob, vos, wl, 1);
+  constexpr int P1 = TN == 4 ? 9 : 5, P2 = TN == 4 ? 7 : 3;
+  constexpr int NA = NCHUNK + (MX ? 2 : 0);                 // fetches in a part-0 issue
+  constexpr int NS = NCHUNK * (4 + TN) / 4 + (MX ? 2 : 0);  // fetches of a whole stage
+  issue_stage<0, MX, TN>(cur, voa, vob, vos, wl, 0);
+  issue_stage<1, MX, TN>(cur, voa, vob, vos, wl, 1);
   wait_vm_lgkm0<NS>();  // stage 0 landed
   lds_barrier();
 
-  v16f acc[TMW][TNW];
-  Frags f0, f1;
-  load_frags<0, MX>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);
+  v16f acc[TMW][TN];
+  Frags<TN> f0, f1;
+  load_frags<0, MX, TN>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);
   while (true) {
     // The next tile's resources: the fetches of the last two K steps go to
     // its first two K tiles (or repeat this tile's, past the last tile), so
@@ -331,12 +339,12 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     const uint32_t nlogical = logical + x_wgs;
     const bool more = nlogical < x_end;
     uint32_t nm0 = m0, nn0 = n0;
-    if (more) tile_coords(g, nlogical, nm0, nn0);
+    if (more) tile_coords<TN>(g, nlogical, nm0, nn0);
     const TileRes nxt_t = resources(nm0, nn0);
 #pragma unroll
     for (int i = 0; i < TMW; ++i)
 #pragma unroll
-      for (int j = 0; j < TNW; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
@@ -356,36 +364,37 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     TileRes RES = own ? cur : nxt_t;                                                           \
     uint32_t FK = own ? (KT) + 2 : (KT) + 2 - nk;                                              \
     pin_res<MX>(RES, FK);                                                                          \
-    load_frags<S, MX>(f1, 1, a_row_off, b_row_off, c10, c11, a_srow, b_srow, sh1);             \
+    load_frags<S, MX, TN>(f1, 1, a_row_off, b_row_off, c10, c11, a_srow, b_srow, sh1);         \
     mfma_range<MX, FA, FB, 0, P1>(acc, f0);                                                    \
-    _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                            \
+    _Pragma("unroll") for (int q = 0; q < P1 - 1; ++q) {                                       \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                       \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TMW + TN) / (P1 - 1), 0);               \
     }                                                                                          \
-    __builtin_amdgcn_sched_group_barrier(0x008, P1 - 8, 0);                                    \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
     __builtin_amdgcn_sched_barrier(0);                                                         \
     wait_vm_lgkm0<63>();                                                                       \
     lds_barrier();                                                                             \
-    issue_part<S, 0, MX>(RES, voa, vob, vos, wl, FK);                                          \
-    mfma_range<MX, FA, FB, P1, 16>(acc, f0);                                                   \
+    issue_part<S, 0, MX, TN>(RES, voa, vob, vos, wl, FK);                                      \
+    mfma_range<MX, FA, FB, P1, NQ>(acc, f0);                                                   \
     mfma_range<MX, FA, FB, 0, P2>(acc, f1);                                                    \
-    _Pragma("unroll") for (int q = 0; q < NA; ++q) {                                           \
+    _Pragma("unroll") for (int q = 0; q < (NA < NQ - P1 + P2 ? NA : NQ - P1 + P2); ++q) {      \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);                                       \
       __builtin_amdgcn_sched_group_barrier(0x001, 3, 1);                                       \
     }                                                                                          \
-    __builtin_amdgcn_sched_group_barrier(0x008, 16 - P1 + P2 - NA, 1);                         \
+    if constexpr (NQ - P1 + P2 > NA)                                                           \
+      __builtin_amdgcn_sched_group_barrier(0x008, NQ - P1 + P2 - NA, 1);                       \
     __builtin_amdgcn_sched_barrier(0);                                                         \
     wait_vm_lgkm0<NA>();                                                                       \
     lds_barrier();                                                                             \
-    load_frags<S ^ 1, MX>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);         \
-    issue_part<S, 1, MX>(RES, voa, vob, vos, wl, FK);                                          \
-    mfma_range<MX, FA, FB, P2, 16>(acc, f1);                                                   \
-    _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                            \
+    load_frags<S ^ 1, MX, TN>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);     \
+    issue_part<S, 1, MX, TN>(RES, voa, vob, vos, wl, FK);                                      \
+    mfma_range<MX, FA, FB, P2, NQ>(acc, f1);                                                   \
+    _Pragma("unroll") for (int q = 0; q < NQ - P2 - 1; ++q) {                                  \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);                                       \
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);                                       \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TMW + TN) / (NQ - P2 - 1), 2);          \
       __builtin_amdgcn_sched_group_barrier(0x001, 3, 2);                                       \
     }                                                                                          \
-    __builtin_amdgcn_sched_group_barrier(0x008, 16 - P2 - 8, 2);                               \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);                                         \
     __builtin_amdgcn_sched_barrier(0);                                                         \
   }
 
@@ -421,13 +430,13 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     int elane = lane;
     asm volatile("" : "+v"(elane));
     const int er = elane & 31, eh = elane >> 5;
-    const bool interior = g.vec_c && bm0 - wm * WM + FBM <= g.M && bn0 - wn * WN + FBN <= g.N;
+    const bool interior = g.vec_c && bm0 - wm * WM + FBM <= g.M && bn0 - wn * WN + TBN <= g.N;
     gbyte* const cw = cbase + (bm0 * ldc + bn0) * ESZ;  // wave-uniform
     const uint32_t lrow = (uint32_t)er * (uint32_t)ldc * ESZ;  // this lane's row offset in bytes
 #pragma unroll
     for (int i = 0; i < TMW; ++i) {
 #pragma unroll
-      for (int j = 0; j < TNW; ++j) {
+      for (int j = 0; j < TN; ++j) {
         u32x4 piece[4];  // bf16: pieces 0, 1 used; fp32: 4 pieces
         int pcol[4];     // column of each piece within the 128-column block
         if constexpr (OUT_BF16) {
@@ -493,7 +502,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     m0 = nm0;
     n0 = nn0;
     cur = nxt_t;
-    load_frags<0, MX>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);
+    load_frags<0, MX, TN>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);
   }
 }
 
@@ -510,21 +519,28 @@ int device_cu_count() {
 }
 
 template <bool MX, int FA, int FB>
-void launch_fast_cfg(const FastArgs& g, bool out_bf16, hipStream_t st) {
+void launch_fast_cfg(const FastArgs& g, bool out_bf16, int tn, hipStream_t st) {
   const int64_t tiles = g.tiles_m * g.tiles_n;
   const unsigned grid = (unsigned)(tiles < g.max_wgs ? tiles : g.max_wgs);
-  if (out_bf16)
-    hipLaunchKernelGGL((gemm_fast_kernel<MX, FA, FB, true>), dim3(grid), dim3(256), 0, st, g);
-  else
-    hipLaunchKernelGGL((gemm_fast_kernel<MX, FA, FB, false>), dim3(grid), dim3(256), 0, st, g);
+  if (tn == 4) {
+    if (out_bf16)
+      hipLaunchKernelGGL((gemm_fast_kernel<MX, FA, FB, true, 4>), dim3(grid), dim3(256), 0, st, g);
+    else
+      hipLaunchKernelGGL((gemm_fast_kernel<MX, FA, FB, false, 4>), dim3(grid), dim3(256), 0, st, g);
+  } else {
+    if (out_bf16)
+      hipLaunchKernelGGL((gemm_fast_kernel<MX, FA, FB, true, 2>), dim3(grid), dim3(256), 0, st, g);
+    else
+      hipLaunchKernelGGL((gemm_fast_kernel<MX, FA, FB, false, 2>), dim3(grid), dim3(256), 0, st, g);
+  }
 }
 
 template <bool MX>
-void launch_fast_fmt(const FastArgs& g, int fa, int fb, bool out_bf16, hipStream_t st) {
-  if (fa == kE4M3 && fb == kE4M3) launch_fast_cfg<MX, kE4M3, kE4M3>(g, out_bf16, st);
-  else if (fa == kE5M2 && fb == kE4M3) launch_fast_cfg<MX, kE5M2, kE4M3>(g, out_bf16, st);
-  else if (fa == kE4M3 && fb == kE5M2) launch_fast_cfg<MX, kE4M3, kE5M2>(g, out_bf16, st);
-  else launch_fast_cfg<MX, kE5M2, kE5M2>(g, out_bf16, st);
+void launch_fast_fmt(const FastArgs& g, int fa, int fb, bool out_bf16, int tn, hipStream_t st) {
+  if (fa == kE4M3 && fb == kE4M3) launch_fast_cfg<MX, kE4M3, kE4M3>(g, out_bf16, tn, st);
+  else if (fa == kE5M2 && fb == kE4M3) launch_fast_cfg<MX, kE5M2, kE4M3>(g, out_bf16, tn, st);
+  else if (fa == kE4M3 && fb == kE5M2) launch_fast_cfg<MX, kE4M3, kE5M2>(g, out_bf16, tn, st);
+  else launch_fast_cfg<MX, kE5M2, kE5M2>(g, out_bf16, tn, st);
 }
 
 }  // namespace
@@ -532,7 +548,7 @@ void launch_fast_fmt(const FastArgs& g, int fa, int fb, bool out_bf16, hipStream
 bool launch_scaled_gemm_fast(const uint8_t* a, int fa, bool mx, const void* sa, const uint8_t* b, int fb,
                              const void* sb, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
                              void* c, int c_dtype, int64_t ldc, hipStream_t st) {
-  // eligibility: whole 128-K tiles, 16-byte rows, 32-bit chunk offsets, enough tiles
+  // eligibility: whole 128-K tiles, 16-byte rows, 32-bit buffer offsets, enough tiles
   if (K <= 0 || K % (2 * FBK) != 0) return false;
   if ((uintptr_t)a % 16 || (uintptr_t)b % 16 || lda % 16 || ldb % 16) return false;
   if (M * lda >= (int64_t)1 << 32 || N * ldb >= (int64_t)1 << 32) return false;
@@ -543,15 +559,41 @@ bool launch_scaled_gemm_fast(const uint8_t* a, int fa, bool mx, const void* sa, 
   g.a = a; g.b = b; g.sa = sa; g.sb = sb;
   g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.c = c;
   const bool out_bf16 = (c_dtype == 1);
+  const int esz = out_bf16 ? 2 : 4;
   // 16-byte row-segment stores need 16-byte aligned rows
-  g.vec_c = ((uintptr_t)c % 16 == 0) && ((ldc * (out_bf16 ? 2 : 4)) % 16 == 0);
+  g.vec_c = ((uintptr_t)c % 16 == 0) && ((ldc * esz) % 16 == 0);
   g.tiles_m = tiles_m;
   g.tiles_n = tiles_n;
   g.max_wgs = device_cu_count();
-  if (mx)
-    launch_fast_fmt<true>(g, fa, fb, out_bf16, st);
-  else
-    launch_fast_fmt<false>(g, fa, fb, out_bf16, st);
+  auto launch = [&](const FastArgs& ga, int tn) {
+    if (mx)
+      launch_fast_fmt<true>(ga, fa, fb, out_bf16, tn, st);
+    else
+      launch_fast_fmt<false>(ga, fa, fb, out_bf16, tn, st);
+  };
+  // A last round that would leave at least half of the workgroups idle, made
+  // of whole tile-rows: those rows run as a second launch of 256 x 128 tiles
+  // (twice as many, each half the work; every output element is computed the
+  // same way, so the results do not change).
+  const int64_t T = tiles_m * tiles_n, G = g.max_wgs, R = T % G;
+  if (T > G && R > 0 && 2 * R <= G && R % tiles_n == 0) {
+    const int64_t tail_rows = R / tiles_n;
+    const int64_t m_main = (tiles_m - tail_rows) * FBM;
+    FastArgs gm = g;
+    gm.M = m_main;
+    gm.tiles_m = tiles_m - tail_rows;
+    launch(gm, 4);
+    FastArgs gt = g;
+    gt.a = a + m_main * lda;
+    gt.c = reinterpret_cast<uint8_t*>(c) + m_main * ldc * esz;
+    if (mx) gt.sa = reinterpret_cast<const uint8_t*>(sa) + m_main * (K / 32);
+    gt.M = M - m_main;
+    gt.tiles_m = tail_rows;
+    gt.tiles_n = (N + 127) / 128;
+    launch(gt, 2);
+  } else {
+    launch(g, 4);
+  }
   return true;
 }
 

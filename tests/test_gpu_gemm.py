@@ -338,6 +338,42 @@ def test_large_tile_persistent_edge_tiles(q, out):
     assert np.array_equal(y, want)
 
 
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_large_tile_partial_last_round(q, out):
+    """56 x 16 tiles of 256 x 256 (a ragged last tile-row): on a 256-CU device
+    the last 128 tiles are half a round, and whole tile-rows, so they run as a
+    second launch of 256 x 128 tiles.  Integer-valued operands make the result
+    exact in binary32, on both launches."""
+    M, N, K = 14336 - 36, 4096, 512
+    g = workloads.generator(54)
+    ia = g.integers(-15, 16, (M, K))
+    ib = g.integers(-15, 16, (N, K))
+    qa = oracle.encode(ia.astype(np.float32), "e4m3")
+    qb = oracle.encode(ib.astype(np.float32), "e5m2")  # rounds to integers of E5M2
+    da = oracle.decode_table("e4m3")[qa].astype(np.float64)
+    db = oracle.decode_table("e5m2")[qb].astype(np.float64)
+    exact = da @ db.T
+    y = gemm(q, to_dev(qa), 0, 0, dscal(1.0), to_dev(qb), 1, 0, dscal(1.0), out=out)
+    want = exact if out == "f32" else f32_to_bf16_rne_f64(exact)
+    assert np.array_equal(y, want)
+
+
+def test_large_tile_mx_partial_last_round(q):
+    """MXFP8 on the same tile grid: the E8M0 rows of the last tile-rows come
+    from the offset scale block of the second launch."""
+    M, N, K = 14336 - 20, 4096, 512
+    g = workloads.generator(55)
+    ia = g.integers(-8, 9, (M, K))
+    ib = g.integers(-8, 9, (N, K))
+    qa = oracle.encode(ia.astype(np.float32), "e4m3")
+    qb = oracle.encode(ib.astype(np.float32), "e4m3")
+    ea = g.integers(125, 130, (M, K // 32)).astype(np.uint8)
+    eb = g.integers(125, 130, (N, K // 32)).astype(np.uint8)
+    ref = oracle.gemm_mx(qa, "e4m3", ea, qb, "e4m3", eb)
+    y = gemm(q, to_dev(qa), 0, q.MXFP8, to_dev(ea), to_dev(qb), 0, q.MXFP8, to_dev(eb), out="bf16")
+    assert np.array_equal(y, f32_to_bf16_rne_f64(ref))
+
+
 def test_large_tile_mx_persistent_edge_tiles(q):
     """MXFP8 through the persistent path with ragged M and N and several
     tiles per workgroup: power-of-two block scales on integer codes keep every

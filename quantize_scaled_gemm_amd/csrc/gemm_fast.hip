@@ -320,7 +320,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
   uint32_t m0, n0;
   tile_coords<TN>(g, logical, m0, n0);
   TileRes cur = resources(m0, n0);
-  constexpr int P1 = TN == 4 ? 9 : 5, P2 = TN == 4 ? 7 : 3;
+  constexpr int P1 = TN == 4 ? 8 : 5, P2 = TN == 4 ? 8 : 3;
   constexpr int NA = NCHUNK + (MX ? 2 : 0);                 // fetches in a part-0 issue
   constexpr int NS = NCHUNK * (4 + TN) / 4 + (MX ? 2 : 0);  // fetches of a whole stage
   issue_stage<0, MX, TN>(cur, voa, vob, vos, wl, 0);

@@ -415,10 +415,12 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
 
     // ---- epilogue: scale, convert, store straight from registers ----
     // In a 32 x 32 accumulator tile, lane l holds row l % 32 and, for group
-    // g = 0..3, columns 8g + 4(l / 32) + 0..3.  For bf16 a lane swap between
-    // the halves (v_permlane32_swap) of groups 2p and 2p + 1 gives every lane
-    // 8 consecutive columns (16 bytes): lanes l and l + 32 then write one
-    // 32-byte piece of row l % 32.  fp32 groups are 16 bytes already.
+    // g = 0..3, columns 8g + 4(l / 32) + 0..3.  For bf16 a swap between the
+    // lane halves (v_permlane32_swap) of groups 2p and 2p + 1 gives every lane
+    // 8 consecutive columns (16 bytes); fp32 groups are 16 bytes already.  A
+    // second swap between lanes l and l + 16 (v_permlane16_swap) of two such
+    // pieces makes 4 lanes hold 64 contiguous bytes of one row, so every store
+    // writes 16 rows x 64 bytes.
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
     // tile coordinates made opaque here, so that no address below is
     // computed ahead of the K loop and kept live across it
@@ -432,13 +434,17 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     const int er = elane & 31, eh = elane >> 5;
     const bool interior = g.vec_c && bm0 - wm * WM + FBM <= g.M && bn0 - wn * WN + TBN <= g.N;
     gbyte* const cw = cbase + (bm0 * ldc + bn0) * ESZ;  // wave-uniform
-    const uint32_t lrow = (uint32_t)er * (uint32_t)ldc * ESZ;  // this lane's row offset in bytes
+    // After the swaps below, a store writes 16 rows x 64 contiguous bytes:
+    // lane l holds row (l % 16) (+16 for the second store of a pair) and the
+    // 16-byte piece pidx = l / 32 + 2 ((l / 16) % 2) of the pair's 64 bytes.
+    const int r16 = elane & 15, pidx = eh + 2 * ((elane >> 4) & 1);
+    const uint32_t loff = ((uint32_t)r16 * (uint32_t)ldc * ESZ) + (uint32_t)pidx * 16;
+    constexpr int NPAIR = OUT_BF16 ? 1 : 2;  // 64-byte column pairs per 32 x 32 tile
 #pragma unroll
     for (int i = 0; i < TMW; ++i) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        u32x4 piece[4];  // bf16: pieces 0, 1 used; fp32: 4 pieces
-        int pcol[4];     // column of each piece within the 128-column block
+        u32x4 lo[2], hi[2];  // per pair: the 16-byte pieces before / after the row swap
         if constexpr (OUT_BF16) {
           uint32_t pk[4][2];
 #pragma unroll
@@ -448,44 +454,57 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
             pk[gq][0] = pack_bf16x2(v0, v1);
             pk[gq][1] = pack_bf16x2(v2, v3);
           }
+          // lane halves: lane l gets columns 8h .. 8h+7 (lo) and 16 + 8h .. (hi)
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
             const auto s0 = __builtin_amdgcn_permlane32_swap(pk[2 * p][0], pk[2 * p + 1][0], false, false);
             const auto s1 = __builtin_amdgcn_permlane32_swap(pk[2 * p][1], pk[2 * p + 1][1], false, false);
-            piece[p] = u32x4{s0[0], s1[0], s0[1], s1[1]};
-            pcol[p] = j * 32 + 16 * p + 8 * eh;
+            (p == 0 ? lo[0] : hi[0]) = u32x4{s0[0], s1[0], s0[1], s1[1]};
           }
         } else {
 #pragma unroll
           for (int gq = 0; gq < 4; ++gq) {
             const float v0 = acc_read(acc[i][j][gq * 4 + 0]) * alpha, v1 = acc_read(acc[i][j][gq * 4 + 1]) * alpha;
             const float v2 = acc_read(acc[i][j][gq * 4 + 2]) * alpha, v3 = acc_read(acc[i][j][gq * 4 + 3]) * alpha;
-            piece[gq] = u32x4{__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2), __float_as_uint(v3)};
-            pcol[gq] = j * 32 + 8 * gq + 4 * eh;
+            const u32x4 w = {__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2), __float_as_uint(v3)};
+            ((gq & 1) ? hi[gq >> 1] : lo[gq >> 1]) = w;
           }
         }
-        constexpr int NP = OUT_BF16 ? 2 : 4;
-        constexpr int PE = 16 / ESZ;  // elements per piece
+        // row swap: lanes 0-15 give their hi piece to lanes 16-31 for their lo
+        // piece (and 32-47 / 48-63 alike), so that x holds rows 0-15 and y rows 16-31
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          gbyte* const cp = cw + (int64_t)(i * 32) * ldc * ESZ + lrow + pcol[p] * ESZ;
-          if (interior) {
-            *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(cp) = piece[p];
-          } else {
-            const int m = (int)bm0 + i * 32 + er;
-            const int n = (int)bn0 + pcol[p];
-            if (m < g.M) {
-              if (g.vec_c && n + PE <= g.N) {
-                *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(cp) = piece[p];
-              } else {
+        for (int pr = 0; pr < NPAIR; ++pr) {
+          u32x4 x, y;
 #pragma unroll
-                for (int e = 0; e < PE; ++e) {
-                  if (n + e < g.N) {
-                    if constexpr (OUT_BF16)
-                      reinterpret_cast<__attribute__((address_space(1))) uint16_t*>(cp)[e] =
-                          (uint16_t)(piece[p][e >> 1] >> (16 * (e & 1)));
-                    else
-                      reinterpret_cast<__attribute__((address_space(1))) uint32_t*>(cp)[e] = piece[p][e];
+          for (int d = 0; d < 4; ++d) {
+            const auto sw = __builtin_amdgcn_permlane16_swap(lo[pr][d], hi[pr][d], false, false);
+            x[d] = sw[0];
+            y[d] = sw[1];
+          }
+          const int cb = j * 32 * ESZ + pr * 64;  // byte column of the pair in the wave's block
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const u32x4 v = half ? y : x;
+            gbyte* const cp = cw + (int64_t)(i * 32 + 16 * half) * ldc * ESZ + cb + loff;
+            if (interior) {
+              *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(cp) = v;
+            } else {
+              constexpr int PE = 16 / ESZ;  // elements per piece
+              const int m = (int)bm0 + i * 32 + 16 * half + r16;
+              const int n = (int)bn0 + cb / ESZ + pidx * PE;
+              if (m < g.M) {
+                if (g.vec_c && n + PE <= g.N) {
+                  *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(cp) = v;
+                } else {
+#pragma unroll
+                  for (int e = 0; e < PE; ++e) {
+                    if (n + e < g.N) {
+                      if constexpr (OUT_BF16)
+                        reinterpret_cast<__attribute__((address_space(1))) uint16_t*>(cp)[e] =
+                            (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+                      else
+                        reinterpret_cast<__attribute__((address_space(1))) uint32_t*>(cp)[e] = v[e];
+                    }
                   }
                 }
               }

@@ -19,6 +19,14 @@ __device__ __forceinline__ u32x4 ld_stream16(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 8-byte streaming store (written once, not read again by this kernel).
+__device__ __forceinline__ void st_stream8(void* p, uint32_t lo, uint32_t hi) {
+  const u32x2 v = {lo, hi};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+}
+
 constexpr int kE4M3 = 0;
 constexpr int kE5M2 = 1;
 

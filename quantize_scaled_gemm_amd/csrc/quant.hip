@@ -9,13 +9,15 @@
 //   * Global loads are 16-byte (8 bf16 or 4 fp32) row segments: 16 lanes
 //     cover a 256-byte row of bf16, fully coalesced.
 //   * The row-wise copy Q is encoded with the 8 values of a row grouped, and
-//     stored straight from registers (8 bytes per lane, 128 contiguous bytes
-//     per row segment).
+//     stored straight from registers with non-temporal stores (8 bytes per
+//     lane, 128 contiguous bytes per row segment).
 //   * The column-wise copy is encoded with the 8 values of a column grouped,
-//     which is already its transposed byte order; each lane writes two 8-byte
-//     pieces per column into an LDS tile [col][row] (stride 136 bytes, 8-byte
-//     slots swizzled by slot ^ tx so the writes of a half-wave hit distinct
-//     banks), and the tile is read back as 16-byte chunks of 16 consecutive
+//     which is already its transposed byte order (where both copies share
+//     one scale -- per-tensor and 128x128 -- the row codes are byte-transposed
+//     in registers with v_perm_b32 instead of being encoded again); each lane
+//     writes two 8-byte pieces per column into an LDS tile [col][row] (stride
+//     136 bytes, 8-byte slots swizzled by slot ^ tx so the writes of a
+//     half-wave hit distinct banks), and the tile is read back as 16-byte chunks of 16 consecutive
 //     rows of one column and stored to QT: 8 lanes cover a 128-byte run.
 //   * Block maxima: 1x32 row blocks are 4 lanes (xor 1, 2); 32x1 column
 //     blocks are the 4 row-groups of one wave (xor 16, 32); 1x128 row blocks
@@ -236,6 +238,22 @@ struct Block8<float> {
   }
 };
 
+// 4 x 4 byte transpose: a..d are four rows of four bytes (byte k = column
+// k); o0..o3 are the four columns (byte k = row k).  Eight v_perm_b32: four
+// interleave the rows in pairs, four gather the columns.
+__device__ __forceinline__ void transpose4x4_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                                   uint32_t& o0, uint32_t& o1, uint32_t& o2, uint32_t& o3) {
+  // v_perm_b32(hi, lo, sel): selector byte values 0-3 pick bytes of lo, 4-7 of hi
+  const uint32_t ab01 = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
+  const uint32_t ab23 = __builtin_amdgcn_perm(b, a, 0x07030602u);  // a2 b2 a3 b3
+  const uint32_t cd01 = __builtin_amdgcn_perm(d, c, 0x05010400u);  // c0 d0 c1 d1
+  const uint32_t cd23 = __builtin_amdgcn_perm(d, c, 0x07030602u);  // c2 d2 c3 d3
+  o0 = __builtin_amdgcn_perm(cd01, ab01, 0x05040100u);             // a0 b0 c0 d0
+  o1 = __builtin_amdgcn_perm(cd01, ab01, 0x07060302u);             // a1 b1 c1 d1
+  o2 = __builtin_amdgcn_perm(cd23, ab23, 0x05040100u);             // a2 b2 c2 d2
+  o3 = __builtin_amdgcn_perm(cd23, ab23, 0x07060302u);             // a3 b3 c3 d3
+}
+
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint32_t canon(uint32_t m) { return m > 0x7F800000u ? 0x7FC00000u : m; }
 
@@ -357,32 +375,53 @@ __global__ __launch_bounds__(256) void tile_kernel(TileArgs a) {
     }
 
     // ---- row-wise copy ------------------------------------------------------
-    if (a.q) {
+    // Where the row and column copies share one scale (per-tensor, 128x128),
+    // the column codes are the row codes transposed, so they are computed
+    // once and transposed as bytes in registers.
+    constexpr bool SAME_SCALE = (MODE == MODE_TENSOR || MODE == MODE_B128X128);
+    uint32_t rq[8][2];
+    if (SAME_SCALE || a.q) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float s = rs[j];
-        uint32_t d0 = enc4<FMT>(b.at(j, 0) * s, b.at(j, 1) * s, b.at(j, 2) * s, b.at(j, 3) * s);
-        uint32_t d1 = enc4<FMT>(b.at(j, 4) * s, b.at(j, 5) * s, b.at(j, 6) * s, b.at(j, 7) * s);
+        rq[j][0] = enc4<FMT>(b.at(j, 0) * s, b.at(j, 1) * s, b.at(j, 2) * s, b.at(j, 3) * s);
+        rq[j][1] = enc4<FMT>(b.at(j, 4) * s, b.at(j, 5) * s, b.at(j, 6) * s, b.at(j, 7) * s);
+      }
+    }
+    if (a.q) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
         if (full) {
-          *reinterpret_cast<uint2*>(a.q + (r + j) * a.cols + c) = make_uint2(d0, d1);
+          st_stream8(a.q + (r + j) * a.cols + c, rq[j][0], rq[j][1]);
         } else if (r + j < a.rows) {
 #pragma unroll
           for (int i = 0; i < 8; ++i)
-            if (c + i < a.cols) a.q[(r + j) * a.cols + c + i] = (uint8_t)(((i < 4 ? d0 : d1) >> (8 * (i & 3))) & 0xFF);
+            if (c + i < a.cols) a.q[(r + j) * a.cols + c + i] = (uint8_t)((rq[j][i >> 2] >> (8 * (i & 3))) & 0xFF);
         }
       }
     }
 
     // ---- column-wise copy through the LDS transpose tile --------------------
     if (a.qt) {
+      uint32_t cq[8][2];  // column i: rows 0-3 in cq[i][0], rows 4-7 in cq[i][1]
+      if constexpr (SAME_SCALE) {
+        transpose4x4_bytes(rq[0][0], rq[1][0], rq[2][0], rq[3][0], cq[0][0], cq[1][0], cq[2][0], cq[3][0]);
+        transpose4x4_bytes(rq[4][0], rq[5][0], rq[6][0], rq[7][0], cq[0][1], cq[1][1], cq[2][1], cq[3][1]);
+        transpose4x4_bytes(rq[0][1], rq[1][1], rq[2][1], rq[3][1], cq[4][0], cq[5][0], cq[6][0], cq[7][0]);
+        transpose4x4_bytes(rq[4][1], rq[5][1], rq[6][1], rq[7][1], cq[4][1], cq[5][1], cq[6][1], cq[7][1]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float s = cs[i];
+          cq[i][0] = enc4<FMT>(b.at(0, i) * s, b.at(1, i) * s, b.at(2, i) * s, b.at(3, i) * s);
+          cq[i][1] = enc4<FMT>(b.at(4, i) * s, b.at(5, i) * s, b.at(6, i) * s, b.at(7, i) * s);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float s = cs[i];
-        uint32_t d0 = enc4<FMT>(b.at(0, i) * s, b.at(1, i) * s, b.at(2, i) * s, b.at(3, i) * s);
-        uint32_t d1 = enc4<FMT>(b.at(4, i) * s, b.at(5, i) * s, b.at(6, i) * s, b.at(7, i) * s);
         const int col = tx * 8 + i;
         const int slot = ty ^ tx;
-        *reinterpret_cast<uint2*>(lds_qt + col * QT_STRIDE + slot * 8) = make_uint2(d0, d1);
+        *reinterpret_cast<uint2*>(lds_qt + col * QT_STRIDE + slot * 8) = make_uint2(cq[i][0], cq[i][1]);
       }
       __syncthreads();
 #pragma unroll

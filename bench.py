@@ -253,6 +253,35 @@ def other_recipes(torch, q, dev):
                              "quantize_weight_ms": round(ms_qw, 4),
                              "quantize_weight_GB/s": round((4.0 + 8.0 / 16384) * W.numel() / ms_qw / 1e6, 1),
                              "fprop_TFLOP/s": round(gemm_flops(M, N, K) / ms_f / 1e9, 1)}
+    del X, W, qx, qw, Y
+
+    # fp32 master weights -> FP8 (W2 14336 x 4096): tensorwise (amax, scale,
+    # cast + transpose: 4 + 4 + 1 + 1 B/elt) and MXFP8 (4 + 1 + 1 + 2/32 B/elt)
+    Wm = torch.from_numpy(workloads.normal([70, 0], (F, H), 0.02, "f32")).to(dev)
+    wq, wqt = torch.empty((F, H), **u8), torch.empty((H, F), **u8)
+    ws = torch.zeros(3, device=dev)
+    ms_t = time_fn(torch, lambda: q.qsg_quantize(Wm, q.TENSORWISE, q.E4M3, q=wq, s=ws, qt=wqt))
+    ws_mx, wst_mx = torch.empty((F, H // 32), **u8), torch.empty((H, F // 32), **u8)
+    ms_m = time_fn(torch, lambda: q.qsg_quantize(Wm, q.MXFP8, q.E4M3, q=wq, s=ws_mx, qt=wqt, st=wst_mx))
+    out["master_weights_fp32_14336x4096"] = {
+        "tensorwise_ms": round(ms_t, 4), "tensorwise_GB/s": round(10.0 * Wm.numel() / ms_t / 1e6, 1),
+        "mxfp8_ms": round(ms_m, 4), "mxfp8_GB/s": round((6.0 + 2.0 / 32) * Wm.numel() / ms_m / 1e6, 1)}
+    del Wm, wq, wqt, ws_mx, wst_mx
+
+    # wgrad accumulated into an fp32 main gradient: dW [4096 x 4096] +=
+    # dY^T X over 32768 tokens (E5M2 x E4M3), next to the same GEMM with bf16 out
+    Tk = 32768
+    a_t = torch.randint(0, 0x7B, (H, Tk), dtype=torch.uint8, device=dev)  # finite E5M2 codes
+    b_t = torch.randint(0, 0x7E, (H, Tk), dtype=torch.uint8, device=dev)  # finite E4M3 codes
+    one = torch.ones(1, device=dev)
+    main_grad = torch.zeros((H, H), device=dev)
+    dw16 = torch.empty((H, H), dtype=torch.bfloat16, device=dev)
+    T = q.TENSORWISE
+    ms_acc = time_fn(torch, lambda: q.qsg_scaled_gemm_accumulate(a_t, q.E5M2, T, one, b_t, q.E4M3, T, one, main_grad))
+    ms_bf = time_fn(torch, lambda: q.qsg_scaled_gemm(a_t, q.E5M2, T, one, b_t, q.E4M3, T, one, dw16))
+    gfl = gemm_flops(H, H, Tk)
+    out["wgrad_main_grad_fp32_4096"] = {"accumulate_TFLOP/s": round(gfl / ms_acc / 1e9, 1),
+                                        "bf16_out_TFLOP/s": round(gfl / ms_bf / 1e9, 1)}
     return out
 
 

@@ -211,6 +211,25 @@ int qsg_scaled_gemm(const uint8_t* a, int fa, int ka, const void* sa,
                     int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
                     void* c, int c_dtype, int64_t ldc, void* stream);
 
+/* Scaled FP8 GEMM accumulated into an fp32 matrix: the weight-gradient
+ * accumulation into fp32 main gradients ("Low-Precision Training Guide",
+ * precision-aware optimizer knob --main-grads-dtype fp32; --fp8-wgrad keeps
+ * the wgrad GEMM itself in FP8):
+ *
+ *     C[m, n] = fp32(C[m, n] + r[m, n]),
+ *     r[m, n] = the fp32 result qsg_scaled_gemm would write (before any
+ *               output rounding to bf16),
+ *
+ * one binary32 addition per element, so micro-batch after micro-batch the
+ * gradient accumulates in C.  Arguments, scale kinds, shapes and alignment
+ * rules are those of qsg_scaled_gemm with c_dtype = QSG_F32; C (M x N, ldc,
+ * 4-byte aligned, caller-owned) is read and written in place.  K == 0 adds
+ * +0.  C must not overlap A, B or the scales. */
+int qsg_scaled_gemm_accumulate(const uint8_t* a, int fa, int ka, const void* sa,
+                               const uint8_t* b, int fb, int kb, const void* sb,
+                               int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                               float* c, int64_t ldc, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -55,5 +55,6 @@ from .gemm import (  # noqa: F401
     gemm_mx,
     gemm_block,
     gemm_exact_fraction,
+    accumulate,
     tolerance_check,
 )

@@ -74,6 +74,15 @@ def gemm_block(qa, fa, sa_inv, qb, fb, sb_inv, b_blocks="128x128"):
     return A @ B.T
 
 
+def accumulate(c_old, product):
+    """Weight-gradient accumulation into fp32 main gradients ("Low-Precision
+    Training Guide", precision-aware optimizer knob --main-grads-dtype fp32):
+    the new C is the old binary32 C plus the GEMM's product, summed in fp64
+    and not rounded (``tolerance_check`` compares the GPU's binary32 result,
+    which rounds that sum once more, with it)."""
+    return np.asarray(c_old, dtype=np.float32).astype(np.float64) + np.asarray(product, dtype=np.float64)
+
+
 def gemm_exact_fraction(qa, fa, a_scale, qb, fb, b_scale):
     """Exact rational GEMM for tiny shapes.
 

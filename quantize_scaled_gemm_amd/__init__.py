@@ -34,6 +34,7 @@ ENTRY_POINTS = (
     "qsg_amax_update",
     "qsg_quantize",
     "qsg_scaled_gemm",
+    "qsg_scaled_gemm_accumulate",
 )
 
 
@@ -76,6 +77,8 @@ def load_library(path=LIB_PATH):
     lib.qsg_quantize.argtypes = [P, I, I64, I64, I64, ctypes.POINTER(Recipe), P, P, P, P, P]
     lib.qsg_scaled_gemm.restype = I
     lib.qsg_scaled_gemm.argtypes = [P, I, I, P, P, I, I, P, I64, I64, I64, I64, I64, P, I, I64, P]
+    lib.qsg_scaled_gemm_accumulate.restype = I
+    lib.qsg_scaled_gemm_accumulate.argtypes = [P, I, I, P, P, I, I, P, I64, I64, I64, I64, I64, P, I64, P]
     _lib = lib
     return lib
 
@@ -179,3 +182,20 @@ def qsg_scaled_gemm(a, fa, ka, sa, b, fb, kb, sb, c, stream=None):
         raise QsgError(f"C is {Mc}x{Nc}, expected {M}x{N}")
     _check(load_library().qsg_scaled_gemm(_ptr(a), fa, ka, _ptr(sa), _ptr(b), fb, kb, _ptr(sb), M, N, K,
                                           lda, ldb, _ptr(c), _dtype_code(c), ldc, _stream(stream)))
+
+
+def qsg_scaled_gemm_accumulate(a, fa, ka, sa, b, fb, kb, sb, c, stream=None):
+    """C (M x N, fp32) = fp32(C + (A sa)(B sb)^T), in place."""
+    import torch
+
+    M, K, lda = _matrix(a)
+    N, Kb, ldb = _matrix(b)
+    if Kb != K:
+        raise QsgError(f"K mismatch: A has {K}, B has {Kb}")
+    Mc, Nc, ldc = _matrix(c)
+    if (Mc, Nc) != (M, N):
+        raise QsgError(f"C is {Mc}x{Nc}, expected {M}x{N}")
+    if c.dtype != torch.float32:
+        raise QsgError("qsg_scaled_gemm_accumulate accumulates into an fp32 C")
+    _check(load_library().qsg_scaled_gemm_accumulate(_ptr(a), fa, ka, _ptr(sa), _ptr(b), fb, kb, _ptr(sb), M, N,
+                                                     K, lda, ldb, _ptr(c), ldc, _stream(stream)))

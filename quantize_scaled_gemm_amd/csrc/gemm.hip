@@ -51,6 +51,7 @@ struct GemmArgs {
   void* c;
   bool vec_ab;   // 16-byte loads of A and B allowed
   bool vec_c;    // vector stores of C allowed
+  bool accumulate;  // fp32 C only: C = fp32(C + result)
   int64_t tiles_m, tiles_n;
 };
 
@@ -308,12 +309,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         } else {
           float* c = reinterpret_cast<float*>(g.c) + m * g.ldc + n;
           if (g.vec_c && n + 3 < g.N) {
+            if (g.accumulate) {
+              const float4 o = *reinterpret_cast<const float4*>(c);
+              v0 += o.x; v1 += o.y; v2 += o.z; v3 += o.w;
+            }
             *reinterpret_cast<float4*>(c) = make_float4(v0, v1, v2, v3);
           } else {
-            if (n + 0 < g.N) c[0] = v0;
-            if (n + 1 < g.N) c[1] = v1;
-            if (n + 2 < g.N) c[2] = v2;
-            if (n + 3 < g.N) c[3] = v3;
+            if (n + 0 < g.N) c[0] = g.accumulate ? c[0] + v0 : v0;
+            if (n + 1 < g.N) c[1] = g.accumulate ? c[1] + v1 : v1;
+            if (n + 2 < g.N) c[2] = g.accumulate ? c[2] + v2 : v2;
+            if (n + 3 < g.N) c[3] = g.accumulate ? c[3] + v3 : v3;
           }
         }
       }
@@ -342,12 +347,13 @@ void launch_fmt(const GemmArgs& g, int fa, int fb, bool out_bf16, hipStream_t st
 
 void launch_scaled_gemm(const uint8_t* a, int fa, int ka, const void* sa, const uint8_t* b, int fb,
                         int kb, const void* sb, int64_t M, int64_t N, int64_t K, int64_t lda,
-                        int64_t ldb, void* c, int c_dtype, int64_t ldc, hipStream_t st) {
+                        int64_t ldb, void* c, int c_dtype, int64_t ldc, bool accumulate, hipStream_t st) {
   const bool per_tensor = (ka == 0 || ka == 1) && (kb == 0 || kb == 1);
   if ((per_tensor || ka == 2) &&
-      launch_scaled_gemm_fast(a, fa, ka == 2, sa, b, fb, sb, M, N, K, lda, ldb, c, c_dtype, ldc, st))
+      launch_scaled_gemm_fast(a, fa, ka == 2, sa, b, fb, sb, M, N, K, lda, ldb, c, c_dtype, ldc, accumulate, st))
     return;
-  if (ka == 3 && kb == 4 &&
+  // (the 128 x 128 blockwise kernel only writes C; accumulation uses the general kernel)
+  if (ka == 3 && kb == 4 && !accumulate &&
       launch_scaled_gemm_block_fast(a, fa, reinterpret_cast<const float*>(sa), b, fb,
                                     reinterpret_cast<const float*>(sb), true, M, N, K, lda, ldb, c, c_dtype, ldc,
                                     st))
@@ -356,6 +362,7 @@ void launch_scaled_gemm(const uint8_t* a, int fa, int ka, const void* sa, const 
   GemmArgs g{};
   g.a = a; g.b = b; g.sa = sa; g.sb = sb;
   g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.c = c;
+  g.accumulate = accumulate && c_dtype == 0;
   g.vec_ab = ((uintptr_t)a % 16 == 0) && ((uintptr_t)b % 16 == 0) && (lda % 16 == 0) && (ldb % 16 == 0);
   const bool out_bf16 = (c_dtype == 1);
   g.vec_c = out_bf16 ? (((uintptr_t)c % 8 == 0) && (ldc % 4 == 0)) : (((uintptr_t)c % 16 == 0) && (ldc % 4 == 0));

@@ -65,6 +65,7 @@ struct FastArgs {
   int64_t M, N, K, lda, ldb, ldc;
   void* c;
   bool vec_c;
+  bool accumulate;  // fp32 C only: C = fp32(C + result)
   int64_t tiles_m, tiles_n;
   int64_t max_wgs;  // persistent grid: one workgroup per CU
 };
@@ -431,7 +432,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     const int64_t bm0 = (int64_t)em0 + wm * WM, bn0 = (int64_t)en0 + wn * WN;
     int elane = lane;
     asm volatile("" : "+v"(elane));
-    const int er = elane & 31, eh = elane >> 5;
+    const int eh = elane >> 5;
     const bool interior = g.vec_c && bm0 - wm * WM + FBM <= g.M && bn0 - wn * WN + TBN <= g.N;
     gbyte* const cw = cbase + (bm0 * ldc + bn0) * ESZ;  // wave-uniform
     // After the swaps below, a store writes 16 rows x 64 contiguous bytes:
@@ -484,9 +485,16 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
           const int cb = j * 32 * ESZ + pr * 64;  // byte column of the pair in the wave's block
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
-            const u32x4 v = half ? y : x;
+            u32x4 v = half ? y : x;
             gbyte* const cp = cw + (int64_t)(i * 32 + 16 * half) * ldc * ESZ + cb + loff;
             if (interior) {
+              if constexpr (!OUT_BF16) {
+                if (g.accumulate) {
+                  const u32x4 o = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(cp);
+#pragma unroll
+                  for (int d = 0; d < 4; ++d) v[d] = __float_as_uint(__uint_as_float(v[d]) + __uint_as_float(o[d]));
+                }
+              }
               *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(cp) = v;
             } else {
               constexpr int PE = 16 / ESZ;  // elements per piece
@@ -494,16 +502,26 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
               const int n = (int)bn0 + cb / ESZ + pidx * PE;
               if (m < g.M) {
                 if (g.vec_c && n + PE <= g.N) {
+                  if constexpr (!OUT_BF16) {
+                    if (g.accumulate) {
+                      const u32x4 o = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(cp);
+#pragma unroll
+                      for (int d = 0; d < 4; ++d)
+                        v[d] = __float_as_uint(__uint_as_float(v[d]) + __uint_as_float(o[d]));
+                    }
+                  }
                   *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(cp) = v;
                 } else {
 #pragma unroll
                   for (int e = 0; e < PE; ++e) {
                     if (n + e < g.N) {
-                      if constexpr (OUT_BF16)
+                      if constexpr (OUT_BF16) {
                         reinterpret_cast<__attribute__((address_space(1))) uint16_t*>(cp)[e] =
                             (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
-                      else
-                        reinterpret_cast<__attribute__((address_space(1))) uint32_t*>(cp)[e] = v[e];
+                      } else {
+                        auto* ce = reinterpret_cast<__attribute__((address_space(1))) float*>(cp) + e;
+                        *ce = g.accumulate ? *ce + __uint_as_float(v[e]) : __uint_as_float(v[e]);
+                      }
                     }
                   }
                 }
@@ -566,7 +584,7 @@ void launch_fast_fmt(const FastArgs& g, int fa, int fb, bool out_bf16, int tn, h
 
 bool launch_scaled_gemm_fast(const uint8_t* a, int fa, bool mx, const void* sa, const uint8_t* b, int fb,
                              const void* sb, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
-                             void* c, int c_dtype, int64_t ldc, hipStream_t st) {
+                             void* c, int c_dtype, int64_t ldc, bool accumulate, hipStream_t st) {
   // eligibility: whole 128-K tiles, 16-byte rows, 32-bit buffer offsets, enough tiles
   if (K <= 0 || K % (2 * FBK) != 0) return false;
   if ((uintptr_t)a % 16 || (uintptr_t)b % 16 || lda % 16 || ldb % 16) return false;
@@ -578,6 +596,7 @@ bool launch_scaled_gemm_fast(const uint8_t* a, int fa, bool mx, const void* sa, 
   g.a = a; g.b = b; g.sa = sa; g.sb = sb;
   g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.c = c;
   const bool out_bf16 = (c_dtype == 1);
+  g.accumulate = accumulate && !out_bf16;
   const int esz = out_bf16 ? 2 : 4;
   // 16-byte row-segment stores need 16-byte aligned rows
   g.vec_c = ((uintptr_t)c % 16 == 0) && ((ldc * esz) % 16 == 0);

@@ -160,10 +160,9 @@ int qsg_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
   return check_launch(fn);
 }
 
-int qsg_scaled_gemm(const uint8_t* a, int fa, int ka, const void* sa, const uint8_t* b, int fb,
-                    int kb, const void* sb, int64_t M, int64_t N, int64_t K, int64_t lda,
-                    int64_t ldb, void* c, int c_dtype, int64_t ldc, void* stream) {
-  const char* fn = "qsg_scaled_gemm";
+static int scaled_gemm(const char* fn, const uint8_t* a, int fa, int ka, const void* sa, const uint8_t* b,
+                       int fb, int kb, const void* sb, int64_t M, int64_t N, int64_t K, int64_t lda,
+                       int64_t ldb, void* c, int c_dtype, int64_t ldc, bool accumulate, void* stream) {
   if (!valid_fmt(fa) || !valid_fmt(fb)) return fail(QSG_ERR_ARG, "%s: bad fp8 format", fn);
   if (!valid_dtype(c_dtype)) return fail(QSG_ERR_ARG, "%s: bad output dtype", fn);
   if (M < 0 || N < 0 || K < 0) return fail(QSG_ERR_ARG, "%s: negative shape", fn);
@@ -190,8 +189,23 @@ int qsg_scaled_gemm(const uint8_t* a, int fa, int ka, const void* sa, const uint
   }
   if (!sa || !sb) return fail(QSG_ERR_ARG, "%s: null scale", fn);
   if (mode != 1 && (!aligned(sa, 4) || !aligned(sb, 4))) return fail(QSG_ERR_ALIGN, "%s: fp32 scales not aligned", fn);
-  qsg::launch_scaled_gemm(a, fa, ka, sa, b, fb, kb, sb, M, N, K, lda, ldb, c, c_dtype, ldc, as_stream(stream));
+  qsg::launch_scaled_gemm(a, fa, ka, sa, b, fb, kb, sb, M, N, K, lda, ldb, c, c_dtype, ldc, accumulate,
+                          as_stream(stream));
   return check_launch(fn);
+}
+
+int qsg_scaled_gemm(const uint8_t* a, int fa, int ka, const void* sa, const uint8_t* b, int fb,
+                    int kb, const void* sb, int64_t M, int64_t N, int64_t K, int64_t lda,
+                    int64_t ldb, void* c, int c_dtype, int64_t ldc, void* stream) {
+  return scaled_gemm("qsg_scaled_gemm", a, fa, ka, sa, b, fb, kb, sb, M, N, K, lda, ldb, c, c_dtype, ldc, false,
+                     stream);
+}
+
+int qsg_scaled_gemm_accumulate(const uint8_t* a, int fa, int ka, const void* sa, const uint8_t* b, int fb,
+                               int kb, const void* sb, int64_t M, int64_t N, int64_t K, int64_t lda,
+                               int64_t ldb, float* c, int64_t ldc, void* stream) {
+  return scaled_gemm("qsg_scaled_gemm_accumulate", a, fa, ka, sa, b, fb, kb, sb, M, N, K, lda, ldb, c, QSG_F32,
+                     ldc, true, stream);
 }
 
 }  // extern "C"

@@ -22,10 +22,11 @@ void launch_quantize_blocked(const void* x, int dtype, int64_t rows, int64_t col
                              uint8_t* qt, void* st_, hipStream_t st);
 // 256x256x128 direct-to-LDS kernel for per-tensor (mx = false) and MXFP8
 // scales; returns false (and launches nothing) when the problem is not
-// eligible, in which case the general kernel is used.
+// eligible, in which case the general kernel is used.  accumulate (fp32 C
+// only): C = fp32(C + result) instead of C = result.
 bool launch_scaled_gemm_fast(const uint8_t* a, int fa, bool mx, const void* sa, const uint8_t* b, int fb,
                              const void* sb, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
-                             void* c, int c_dtype, int64_t ldc, hipStream_t st);
+                             void* c, int c_dtype, int64_t ldc, bool accumulate, hipStream_t st);
 // 128x128 two-workgroups-per-CU kernel for blockwise scales with 128x128
 // weight blocks (w128; 1x128 activation blocks on A); returns false (and
 // launches nothing) when the problem is not eligible.
@@ -34,6 +35,6 @@ bool launch_scaled_gemm_block_fast(const uint8_t* a, int fa, const float* sa, co
                                    int64_t ldb, void* c, int c_dtype, int64_t ldc, hipStream_t st);
 void launch_scaled_gemm(const uint8_t* a, int fa, int ka, const void* sa, const uint8_t* b, int fb,
                         int kb, const void* sb, int64_t M, int64_t N, int64_t K, int64_t lda,
-                        int64_t ldb, void* c, int c_dtype, int64_t ldc, hipStream_t st);
+                        int64_t ldb, void* c, int c_dtype, int64_t ldc, bool accumulate, hipStream_t st);
 
 }  // namespace qsg

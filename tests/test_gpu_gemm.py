@@ -389,3 +389,76 @@ def test_large_tile_mx_persistent_edge_tiles(q):
     ref = oracle.gemm_mx(qa, "e4m3", ea, qb, "e4m3", eb)
     y = gemm(q, to_dev(qa), 0, q.MXFP8, to_dev(ea), to_dev(qb), 0, q.MXFP8, to_dev(eb), out="f32")
     assert np.array_equal(y, ref)
+
+
+# ---------------------------------------------------------------------------
+# accumulation into fp32 main gradients (qsg_scaled_gemm_accumulate)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,K", [(130, 250, 300), (64, 64, 16), (2048, 4096, 256), (2048 + 100, 4096 - 36, 512)])
+def test_accumulate_integer_exact(q, M, N, K):
+    """Two micro-batches of integer-valued operands accumulated into an
+    integer-valued fp32 C: every sum is an integer below 2^24, so C must be
+    exact (small shapes: general kernel; large: the 256 x 256 kernel, ragged)."""
+    g = workloads.generator(60, M, N, K)
+    c0 = g.integers(-1000, 1001, (M, N)).astype(np.float32)
+    c = to_dev(c0)
+    exact = c0.astype(np.float64)
+    for _ in range(2):
+        ia = g.integers(-8, 9, (M, K))  # every integer in [-8, 8] is exact in E5M2
+        ib = g.integers(-15, 16, (N, K))
+        qa = oracle.encode(ia.astype(np.float32), "e5m2")
+        qb = oracle.encode(ib.astype(np.float32), "e4m3")
+        q.qsg_scaled_gemm_accumulate(to_dev(qa), 1, 0, dscal(1.0), to_dev(qb), 0, 0, dscal(1.0), c)
+        exact = exact + ia.astype(np.float64) @ ib.T.astype(np.float64)
+        assert np.array_equal(to_np(c).astype(np.float64), exact)
+
+
+@pytest.mark.parametrize("kind,M,N,K", [("tensor", 256, 384, 512), ("tensor", 4096 + 64, 4096, 1024),
+                                        ("mx", 160, 96, 1024), ("mx", 4096, 4096 + 64, 512),
+                                        ("block", 256, 384, 1024)])
+def test_accumulate_wgrad_micro_batches(q, kind, M, N, K):
+    """dW (fp32 main gradient, M x N here) accumulated over two micro-batches
+    of wgrad GEMMs (contraction K over the micro-batch's tokens) against the
+    oracle's fp64 chain, to the 1e-2 relative acceptance rule after each."""
+    import torch
+
+    g = workloads.generator(61, M, N, K)
+    c0 = (0.01 * g.standard_normal((M, N))).astype(np.float32)
+    c = to_dev(c0)
+    ref = c0.astype(np.float64)
+    for mb in range(2):
+        dy = workloads.normal([61, mb, 0], (M, K), 1e-3, "f32")
+        x = workloads.normal([61, mb, 1], (N, K), 1.0, "f32")
+        if kind == "tensor":
+            qa, _, _, _, sa = oracle.quantize_tensorwise(dy, "e5m2")
+            qb, _, _, _, sb = oracle.quantize_tensorwise(x, "e4m3")
+            prod = oracle.gemm_per_tensor(qa, "e5m2", sa, qb, "e4m3", sb)
+            q.qsg_scaled_gemm_accumulate(to_dev(qa), 1, 0, dscal(sa), to_dev(qb), 0, 0, dscal(sb), c)
+        elif kind == "mx":
+            qa = oracle.mx_quantize(dy, "e4m3", colwise=False)
+            qb = oracle.mx_quantize(x, "e4m3", colwise=False)
+            prod = oracle.gemm_mx(qa["q"], "e4m3", qa["s"], qb["q"], "e4m3", qb["s"])
+            q.qsg_scaled_gemm_accumulate(to_dev(qa["q"]), 0, q.MXFP8, to_dev(qa["s"]), to_dev(qb["q"]), 0,
+                                         q.MXFP8, to_dev(qb["s"]), c)
+        else:
+            qa = oracle.block_quantize_1x128(dy, "e4m3", colwise=False)
+            qb = oracle.block_quantize_1x128(x, "e4m3", colwise=False)
+            prod = oracle.gemm_block(qa["q"], "e4m3", qa["s"], qb["q"], "e4m3", qb["s"], b_blocks="1x128")
+            q.qsg_scaled_gemm_accumulate(to_dev(qa["q"]), 0, q.BLOCK_1X128, to_dev(qa["s"]), to_dev(qb["q"]), 0,
+                                         q.BLOCK_1X128, to_dev(qb["s"]), c)
+        torch.cuda.synchronize()
+        got = to_np(c).astype(np.float64)
+        ref = oracle.accumulate(np.float32(ref), prod)
+        ok, info = oracle.tolerance_check(got, ref)
+        assert ok, (kind, mb, info)
+        ref = got  # the next micro-batch adds to the binary32 C the GPU holds
+
+
+def test_accumulate_k_zero_keeps_c(q):
+    import torch
+
+    a = torch.empty((64, 0), dtype=torch.uint8, device="cuda")
+    b = torch.empty((32, 0), dtype=torch.uint8, device="cuda")
+    c = torch.full((64, 32), 5.0, device="cuda")
+    q.qsg_scaled_gemm_accumulate(a, 0, 0, dscal(1.0), b, 0, 0, dscal(1.0), c)
+    assert np.all(to_np(c) == 5.0)

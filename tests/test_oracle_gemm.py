@@ -6,7 +6,9 @@
 * the three GEMMs of a Linear (fprop, dgrad, wgrad) built from the quantized
   tensors and their transposed copies agree with the dense products;
 * the acceptance rule rejects a planted error (a wrong sign, a transposed
-  operand, a 2% scale error).
+  operand, a 2% scale error);
+* accumulating into an fp32 C micro-batch by micro-batch equals C plus the
+  product over the concatenated contraction (exact rational brute force).
 """
 
 from fractions import Fraction
@@ -128,3 +130,28 @@ def test_tolerance_rule_rejects_planted_errors():
     import torch
     yb = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
     assert oracle.tolerance_check(yb, ref)[0]
+
+
+def test_accumulate_over_micro_batches_vs_fraction():
+    """Two accumulations of wgrad-shaped products (contraction over the
+    tokens of two micro-batches) into an fp32 C equal C + the product over
+    all tokens, which is one exact rational sum; a planted sign error in the
+    accumulation fails the comparison."""
+    g = np.random.Generator(np.random.PCG64(36))
+    N, K, T = 5, 7, 24  # dW is N x K; each micro-batch has T tokens
+    qdy = [rand_codes(g, (N, T), "e5m2") for _ in range(2)]  # Q(dY)^T of each micro-batch
+    qx = [rand_codes(g, (K, T), "e4m3") for _ in range(2)]   # Q(X)^T
+    c0 = g.standard_normal((N, K)).astype(np.float32)
+    sa, sb = np.float32(0.375), np.float32(2.0 ** -7)
+    c1 = oracle.accumulate(c0, oracle.gemm_per_tensor(qdy[0], "e5m2", sa, qx[0], "e4m3", sb))
+    c = oracle.accumulate(np.float32(c1), oracle.gemm_per_tensor(qdy[1], "e5m2", sa, qx[1], "e4m3", sb))
+    full = oracle.gemm_exact_fraction(np.concatenate(qdy, axis=1), "e5m2", lambda m, k: Fraction(float(sa)),
+                                      np.concatenate(qx, axis=1), "e4m3", lambda n, k: Fraction(float(sb)))
+    exact = as_float([[Fraction(float(c0[i, j])) + full[i][j] for j in range(K)] for i in range(N)])
+    # the roundings: binary32 C between the two accumulations (half an ulp
+    # of c1) and fp64 in the sums (far below that)
+    bound = 2.0 ** -24 * np.abs(c1) + 2.0 ** -40 * (np.abs(exact) + 1)
+    assert np.all(np.abs(c - exact) <= bound)
+    bad = np.asarray(c0, dtype=np.float64) - oracle.gemm_per_tensor(qdy[0], "e5m2", sa, qx[0], "e4m3", sb)
+    bad = oracle.accumulate(np.float32(bad), oracle.gemm_per_tensor(qdy[1], "e5m2", sa, qx[1], "e4m3", sb))
+    assert not np.all(np.abs(bad - exact) <= bound)

@@ -300,24 +300,26 @@ def cpu_baseline(step_flops, step_elems):
     except Exception:  # pragma: no cover - informational only
         blas_threads = 1
 
-    # quantization sample: amax + scale + cast + transpose of all of X and W2
-    # (192M of the step's 814M quantized elements)
-    host = workloads.linear_4096(M, H, F, which=("X", "W2"))
-    xs = workloads.bf16_bits_to_f32(host["X"])
-    w2 = workloads.bf16_bits_to_f32(host["W2"])
+    # quantization sample: amax + scale + cast + transpose of X, W, W2 and dY
+    # (344M of the step's 814M quantized elements)
+    host = workloads.linear_4096(M, H, F, which=("X", "W", "W2", "dY"))
+    ts = {k: workloads.bf16_bits_to_f32(host[k]) for k in ("X", "W", "W2", "dY")}
     del host
+    nq = sum(t.size for t in ts.values())
     t0 = time.perf_counter()
-    qx, _, _, _, sxi = oracle.quantize_tensorwise(xs, "e4m3")
-    qw, _, _, _, swi = oracle.quantize_tensorwise(w2, "e4m3")
+    qx, _, _, _, sxi = oracle.quantize_tensorwise(ts["X"], "e4m3")
+    oracle.quantize_tensorwise(ts["W"], "e4m3")
+    qw, _, _, _, swi = oracle.quantize_tensorwise(ts["W2"], "e4m3")
+    oracle.quantize_tensorwise(ts["dY"], "e5m2")
     tq = time.perf_counter() - t0
-    per_elem = tq / (xs.size + w2.size)
-    del xs, w2
+    per_elem = tq / nq
+    del ts
 
-    # GEMM sample: fp64 product of the dequantized operands, 16384 rows of X
-    # against all of W2 (the first half of the larger Linear's fprop)
-    rows_g = 16384
+    # GEMM sample: fp64 product of the dequantized operands, all 32768 rows
+    # of X against all of W2 (the larger Linear's fprop)
+    rows_g = M
     t0 = time.perf_counter()
-    oracle.gemm_per_tensor(qx[:rows_g], "e4m3", sxi, qw, "e4m3", swi)
+    oracle.gemm_per_tensor(qx, "e4m3", sxi, qw, "e4m3", swi)
     tg = time.perf_counter() - t0
     gemm_rate = gemm_flops(rows_g, F, H) / tg
 
@@ -327,8 +329,8 @@ def cpu_baseline(step_flops, step_elems):
         "unit": "TFLOP/s",
         "cores": int(blas_threads),
         "kind": "oracle",
-        "sample": (f"tensorwise quantize of X {M}x{H} and W2 {F}x{H} ({tq:.2f}s, numpy, 1 thread) and the "
-                   f"fp64 fprop GEMM of {rows_g} rows of X against all of W2 ({tg:.2f}s, BLAS "
+        "sample": (f"tensorwise quantize of X, W, W2 and dY ({nq / 1e6:.0f}M elements, {tq:.2f}s, numpy, "
+                   f"1 thread) and the fp64 fprop GEMM of X ({rows_g} rows) against W2 ({tg:.2f}s, BLAS "
                    f"{blas_threads} threads), extrapolated to the full step's {step_elems/1e6:.0f}M quantized "
                    f"elements and {step_flops/1e12:.2f} TFLOP"),
     }

@@ -282,6 +282,22 @@ def other_recipes(torch, q, dev):
     gfl = gemm_flops(H, H, Tk)
     out["wgrad_main_grad_fp32_4096"] = {"accumulate_TFLOP/s": round(gfl / ms_acc / 1e9, 1),
                                         "bf16_out_TFLOP/s": round(gfl / ms_bf / 1e9, 1)}
+    del a_t, b_t, main_grad, dw16
+
+    # GeLU with its input stored in FP8: h = the FC1 output X W2^T [32768 x 14336]
+    # (~N(0, 1.28)); forward 2 + 2 + 1 B/elt, backward 2 + 1 + 2 B/elt
+    M_ = 32768
+    h = torch.from_numpy(workloads.normal([90, 9], (M_, F), 1.28).view(np.int16)).view(torch.bfloat16).to(dev)
+    da = torch.from_numpy(workloads.normal([90, 10], (M_, F), 1e-3).view(np.int16)).view(torch.bfloat16).to(dev)
+    act = torch.empty_like(h)
+    hq = torch.empty((M_, F), **u8)
+    dh = torch.empty_like(h)
+    sc = torch.full((1,), 448.0 / 8.0, device=dev)
+    si = 1.0 / sc
+    ms_f = time_fn(torch, lambda: q.qsg_act_fp8_store_fwd(h, q.E4M3, sc, act, hq))
+    ms_b = time_fn(torch, lambda: q.qsg_act_fp8_store_bwd(da, q.E4M3, hq, si, dh))
+    out["gelu_fp8_input_store_32768x14336"] = {"fwd_ms": round(ms_f, 4), "fwd_GB/s": round(5.0 * h.numel() / ms_f / 1e6, 1),
+                                               "bwd_ms": round(ms_b, 4), "bwd_GB/s": round(5.0 * h.numel() / ms_b / 1e6, 1)}
     return out
 
 

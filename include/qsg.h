@@ -161,6 +161,35 @@ int qsg_amax_update(float* history_dev, int64_t hist_len, int64_t step,
                     const float* amax_dev, int algo, int fmt, int margin,
                     float* scale_dev, float* scale_inv_dev, void* stream);
 
+/* FP8 store of the MLP activation's input, forward ("Benefits of Using FP8
+ * Precision with MegaDLMs and Required Hardware", configuration field
+ * activation_func_fp8_input_store: the activation's input is kept in FP8 for
+ * backpropagation).  The activation is GeLU, gelu(h) = h * Phi(h) with Phi the
+ * standard normal CDF (erf form; the pages do not name the function).
+ *   h             rows x cols bf16, leading dimension ld (2-byte aligned; the
+ *                 vector path needs h, a 16-byte and q 8-byte aligned with ld
+ *                 and cols multiples of 8).
+ *   scale_dev     in: 1 float, the per-tensor scale of the stored input.
+ *   a             out: rows x cols bf16 (dense), bf16(gelu(h)) rounded to
+ *                 nearest even from a binary32 evaluation.
+ *   q             out: rows x cols FP8 bytes (dense), enc(fp32(h * scale)).
+ *   amax_out_dev  out: 1 float, max |h| (as qsg_amax, for delayed scaling of
+ *                 the stored input), or NULL.
+ * The caller owns every buffer; nothing is allocated. */
+int qsg_act_fp8_store_fwd(const void* h, int64_t rows, int64_t cols, int64_t ld, int fmt,
+                          const float* scale_dev, void* a, uint8_t* q, float* amax_out_dev,
+                          void* stream);
+
+/* Backward of the above: the activation's gradient from the stored FP8 input.
+ *   da            rows x cols bf16 (ld), the gradient of a.
+ *   q             rows x cols FP8 bytes (dense) in format fmt, as written by
+ *                 qsg_act_fp8_store_fwd.
+ *   scale_inv_dev in: 1 float; the input is recovered as h' = fp32(dec(q) * scale_inv).
+ *   dh            out: rows x cols bf16 (dense), bf16(da * gelu'(h')) with
+ *                 gelu'(h) = Phi(h) + h phi(h), phi the standard normal density. */
+int qsg_act_fp8_store_bwd(const void* da, int64_t rows, int64_t cols, int64_t ld, int fmt,
+                          const uint8_t* q, const float* scale_inv_dev, void* dh, void* stream);
+
 /* Quantize one tensor under a recipe, producing the row-wise copy (blocks run
  * along cols, the GEMM contraction dimension of the tensor as stored) and/or
  * the column-wise copy (blocks run along rows, stored transposed so that it

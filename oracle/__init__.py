@@ -12,7 +12,8 @@ Sources, cited per function:
     names (delayed, tensorwise, mxfp8, blockwise), the block shapes, the
     margin knob, the amax history length and compute algorithm.
   * "Benefits of Using FP8 Precision with MegaDLMs and Required Hardware": the
-    E4M3 format flag and the hybrid mode.
+    E4M3 format flag and the hybrid mode; the FP8 store of the MLP
+    activation's input (activation_func_fp8_input_store).
   * "How to reduce cuda memory usage of fp8?" (TransformerEngine issue 1764):
     why a transposed FP8 copy of each operand exists (the backward pass reads
     it).
@@ -57,4 +58,11 @@ from .gemm import (  # noqa: F401
     gemm_exact_fraction,
     accumulate,
     tolerance_check,
+)
+from .activation import (  # noqa: F401
+    gelu,
+    gelu_grad,
+    act_fp8_store_fwd,
+    act_fp8_store_bwd,
+    elementwise_check,
 )

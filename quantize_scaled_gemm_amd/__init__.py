@@ -35,6 +35,8 @@ ENTRY_POINTS = (
     "qsg_quantize",
     "qsg_scaled_gemm",
     "qsg_scaled_gemm_accumulate",
+    "qsg_act_fp8_store_fwd",
+    "qsg_act_fp8_store_bwd",
 )
 
 
@@ -78,6 +80,10 @@ def load_library(path=LIB_PATH):
     lib.qsg_scaled_gemm.restype = I
     lib.qsg_scaled_gemm.argtypes = [P, I, I, P, P, I, I, P, I64, I64, I64, I64, I64, P, I, I64, P]
     lib.qsg_scaled_gemm_accumulate.restype = I
+    lib.qsg_act_fp8_store_fwd.restype = I
+    lib.qsg_act_fp8_store_fwd.argtypes = [P, I64, I64, I64, I, F, P, P, F, P]
+    lib.qsg_act_fp8_store_bwd.restype = I
+    lib.qsg_act_fp8_store_bwd.argtypes = [P, I64, I64, I64, I, P, F, P, P]
     lib.qsg_scaled_gemm_accumulate.argtypes = [P, I, I, P, P, I, I, P, I64, I64, I64, I64, I64, P, I64, P]
     _lib = lib
     return lib
@@ -199,3 +205,21 @@ def qsg_scaled_gemm_accumulate(a, fa, ka, sa, b, fb, kb, sb, c, stream=None):
         raise QsgError("qsg_scaled_gemm_accumulate accumulates into an fp32 C")
     _check(load_library().qsg_scaled_gemm_accumulate(_ptr(a), fa, ka, _ptr(sa), _ptr(b), fb, kb, _ptr(sb), M, N,
                                                      K, lda, ldb, _ptr(c), ldc, _stream(stream)))
+
+
+def qsg_act_fp8_store_fwd(h, fmt, scale, a, q, amax_out=None, stream=None):
+    """a = bf16(gelu(h)); q = FP8 of h * scale (h bf16, a and q dense)."""
+    rows, cols, ld = _matrix(h)
+    if _dtype_code(h) != BF16:
+        raise QsgError("qsg_act_fp8_store_fwd takes a bf16 input")
+    _check(load_library().qsg_act_fp8_store_fwd(_ptr(h), rows, cols, ld, fmt, _ptr(scale), _ptr(a), _ptr(q),
+                                                _ptr(amax_out), _stream(stream)))
+
+
+def qsg_act_fp8_store_bwd(da, fmt, q, scale_inv, dh, stream=None):
+    """dh = bf16(da * gelu'(dec(q) * scale_inv)) (da bf16, q and dh dense)."""
+    rows, cols, ld = _matrix(da)
+    if _dtype_code(da) != BF16:
+        raise QsgError("qsg_act_fp8_store_bwd takes a bf16 gradient")
+    _check(load_library().qsg_act_fp8_store_bwd(_ptr(da), rows, cols, ld, fmt, _ptr(q), _ptr(scale_inv), _ptr(dh),
+                                                _stream(stream)))

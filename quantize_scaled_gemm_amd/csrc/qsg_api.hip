@@ -97,6 +97,35 @@ int qsg_cast_transpose(const void* x, int dtype, int64_t rows, int64_t cols, int
   return check_launch("qsg_cast_transpose");
 }
 
+int qsg_act_fp8_store_fwd(const void* h, int64_t rows, int64_t cols, int64_t ld, int fmt, const float* scale_dev,
+                          void* a, uint8_t* q, float* amax_out_dev, void* stream) {
+  const char* fn = "qsg_act_fp8_store_fwd";
+  int rc = check_matrix(fn, h, QSG_BF16, rows, cols, ld);
+  if (rc) return rc;
+  if (!valid_fmt(fmt)) return fail(QSG_ERR_ARG, "%s: bad fmt %d", fn, fmt);
+  if (!scale_dev) return fail(QSG_ERR_ARG, "%s: null scale", fn);
+  const bool empty = rows == 0 || cols == 0;
+  if (!empty && (!a || !q)) return fail(QSG_ERR_ARG, "%s: null output", fn);
+  if (a && !aligned(a, 2)) return fail(QSG_ERR_ALIGN, "%s: a not aligned to 2 bytes", fn);
+  if (amax_out_dev && !aligned(amax_out_dev, 4)) return fail(QSG_ERR_ALIGN, "%s: amax_out not aligned", fn);
+  qsg::launch_act_fp8_store_fwd(h, rows, cols, ld, fmt, scale_dev, a, q, amax_out_dev, as_stream(stream));
+  return check_launch(fn);
+}
+
+int qsg_act_fp8_store_bwd(const void* da, int64_t rows, int64_t cols, int64_t ld, int fmt, const uint8_t* q,
+                          const float* scale_inv_dev, void* dh, void* stream) {
+  const char* fn = "qsg_act_fp8_store_bwd";
+  int rc = check_matrix(fn, da, QSG_BF16, rows, cols, ld);
+  if (rc) return rc;
+  if (!valid_fmt(fmt)) return fail(QSG_ERR_ARG, "%s: bad fmt %d", fn, fmt);
+  if (!scale_inv_dev) return fail(QSG_ERR_ARG, "%s: null scale_inv", fn);
+  const bool empty = rows == 0 || cols == 0;
+  if (!empty && (!q || !dh)) return fail(QSG_ERR_ARG, "%s: null q or dh", fn);
+  if (dh && !aligned(dh, 2)) return fail(QSG_ERR_ALIGN, "%s: dh not aligned to 2 bytes", fn);
+  qsg::launch_act_fp8_store_bwd(da, rows, cols, ld, fmt, q, scale_inv_dev, dh, as_stream(stream));
+  return check_launch(fn);
+}
+
 int qsg_amax_update(float* history_dev, int64_t hist_len, int64_t step, const float* amax_dev,
                     int algo, int fmt, int margin, float* scale_dev, float* scale_inv_dev,
                     void* stream) {

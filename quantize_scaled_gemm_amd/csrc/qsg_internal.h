@@ -33,6 +33,13 @@ bool launch_scaled_gemm_fast(const uint8_t* a, int fa, bool mx, const void* sa, 
 bool launch_scaled_gemm_block_fast(const uint8_t* a, int fa, const float* sa, const uint8_t* b, int fb,
                                    const float* sb, bool w128, int64_t M, int64_t N, int64_t K, int64_t lda,
                                    int64_t ldb, void* c, int c_dtype, int64_t ldc, hipStream_t st);
+// GeLU of h with the FP8 store of h (forward) and the GeLU gradient from the
+// stored FP8 input (backward); bf16 h / da with leading dimension ld, dense
+// a / dh / q.
+void launch_act_fp8_store_fwd(const void* h, int64_t rows, int64_t cols, int64_t ld, int fmt, const float* scale,
+                              void* a, uint8_t* q, float* amax_out, hipStream_t st);
+void launch_act_fp8_store_bwd(const void* da, int64_t rows, int64_t cols, int64_t ld, int fmt, const uint8_t* q,
+                              const float* scale_inv, void* dh, hipStream_t st);
 void launch_scaled_gemm(const uint8_t* a, int fa, int ka, const void* sa, const uint8_t* b, int fb,
                         int kb, const void* sb, int64_t M, int64_t N, int64_t K, int64_t lda,
                         int64_t ldb, void* c, int c_dtype, int64_t ldc, bool accumulate, hipStream_t st);

@@ -284,6 +284,18 @@ def other_recipes(torch, q, dev):
                                         "bf16_out_TFLOP/s": round(gfl / ms_bf / 1e9, 1)}
     del a_t, b_t, main_grad, dw16
 
+    # wgrad kept in bf16 (--fp8-wgrad False): dW [4096 x 4096] = dY^T X over 32768 tokens
+    dyb = torch.randn((Tk, H), device=dev).mul_(1e-3).to(torch.bfloat16)
+    xb = torch.randn((Tk, H), device=dev).to(torch.bfloat16)
+    dw_bf = torch.empty((H, H), dtype=torch.bfloat16, device=dev)
+    mg = torch.zeros((H, H), device=dev)
+    ms_w16 = time_fn(torch, lambda: q.qsg_wgrad_bf16(dyb, xb, dw_bf))
+    ms_w32 = time_fn(torch, lambda: q.qsg_wgrad_bf16(dyb, xb, mg, accumulate=True))
+    out["wgrad_bf16_4096"] = {"bf16_out_TFLOP/s": round(gfl / ms_w16 / 1e9, 1),
+                              "fp32_accumulate_TFLOP/s": round(gfl / ms_w32 / 1e9, 1),
+                              "frac_of_bf16_peak": round(gfl / ms_w16 / 1e9 / 2500.0, 4)}
+    del dyb, xb, dw_bf, mg
+
     # GeLU with its input stored in FP8: h = the FC1 output X W2^T [32768 x 14336]
     # (~N(0, 1.28)); forward 2 + 2 + 1 B/elt, backward 2 + 1 + 2 B/elt
     M_ = 32768

@@ -190,6 +190,25 @@ int qsg_act_fp8_store_fwd(const void* h, int64_t rows, int64_t cols, int64_t ld,
 int qsg_act_fp8_store_bwd(const void* da, int64_t rows, int64_t cols, int64_t ld, int fmt,
                           const uint8_t* q, const float* scale_inv_dev, void* dh, void* stream);
 
+/* Weight-gradient GEMM kept in bf16 ("Low-Precision Training Guide", knob
+ * --fp8-wgrad False: wgrad in higher precision while fprop and dgrad use FP8):
+ *
+ *     C[n, k] = sum_t dY[t, n] * X[t, k]      (accumulate = 0)
+ *     C[n, k] = fp32(C[n, k] + sum_t ...)     (accumulate = 1, fp32 C only:
+ *                                              the fp32 main gradient)
+ *
+ *   dy  T x N bf16 (tokens x output features), leading dimension lddy;
+ *   x   T x K bf16 (tokens x input features), leading dimension ldx; both
+ *       2-byte aligned (the vector path needs 16-byte aligned rows: bases
+ *       16-byte aligned, lddy and ldx multiples of 8);
+ *   c   N x K, ldc, c_dtype QSG_BF16 (rounded to nearest even) or QSG_F32,
+ *       aligned to its element size; products of bf16 values are exact in
+ *       fp32 and are summed in fp32.
+ * T == 0 writes zeros (or adds +0).  Accumulation into bf16 returns
+ * QSG_ERR_UNSUPPORTED. */
+int qsg_wgrad_bf16(const void* dy, int64_t T, int64_t N, int64_t lddy, const void* x, int64_t K,
+                   int64_t ldx, void* c, int c_dtype, int64_t ldc, int accumulate, void* stream);
+
 /* Quantize one tensor under a recipe, producing the row-wise copy (blocks run
  * along cols, the GEMM contraction dimension of the tensor as stored) and/or
  * the column-wise copy (blocks run along rows, stored transposed so that it

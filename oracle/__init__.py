@@ -57,6 +57,7 @@ from .gemm import (  # noqa: F401
     gemm_block,
     gemm_exact_fraction,
     accumulate,
+    wgrad_bf16,
     tolerance_check,
 )
 from .activation import (  # noqa: F401

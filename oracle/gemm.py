@@ -83,6 +83,14 @@ def accumulate(c_old, product):
     return np.asarray(c_old, dtype=np.float32).astype(np.float64) + np.asarray(product, dtype=np.float64)
 
 
+def wgrad_bf16(dy, x):
+    """Weight gradient kept in higher precision ("Low-Precision Training
+    Guide", knob --fp8-wgrad False): dW[n, k] = sum over tokens t of
+    dY[t, n] * X[t, k], from the bf16 values of dY (T x N) and X (T x K)
+    given as binary32 arrays, summed in fp64 (not rounded)."""
+    return np.asarray(dy, dtype=np.float64).T @ np.asarray(x, dtype=np.float64)
+
+
 def gemm_exact_fraction(qa, fa, a_scale, qb, fb, b_scale):
     """Exact rational GEMM for tiny shapes.
 

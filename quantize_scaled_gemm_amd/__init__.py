@@ -37,6 +37,7 @@ ENTRY_POINTS = (
     "qsg_scaled_gemm_accumulate",
     "qsg_act_fp8_store_fwd",
     "qsg_act_fp8_store_bwd",
+    "qsg_wgrad_bf16",
 )
 
 
@@ -80,6 +81,8 @@ def load_library(path=LIB_PATH):
     lib.qsg_scaled_gemm.restype = I
     lib.qsg_scaled_gemm.argtypes = [P, I, I, P, P, I, I, P, I64, I64, I64, I64, I64, P, I, I64, P]
     lib.qsg_scaled_gemm_accumulate.restype = I
+    lib.qsg_wgrad_bf16.restype = I
+    lib.qsg_wgrad_bf16.argtypes = [P, I64, I64, I64, P, I64, I64, P, I, I64, I, P]
     lib.qsg_act_fp8_store_fwd.restype = I
     lib.qsg_act_fp8_store_fwd.argtypes = [P, I64, I64, I64, I, F, P, P, F, P]
     lib.qsg_act_fp8_store_bwd.restype = I
@@ -223,3 +226,18 @@ def qsg_act_fp8_store_bwd(da, fmt, q, scale_inv, dh, stream=None):
         raise QsgError("qsg_act_fp8_store_bwd takes a bf16 gradient")
     _check(load_library().qsg_act_fp8_store_bwd(_ptr(da), rows, cols, ld, fmt, _ptr(q), _ptr(scale_inv), _ptr(dh),
                                                 _stream(stream)))
+
+
+def qsg_wgrad_bf16(dy, x, c, accumulate=False, stream=None):
+    """C (N x K) = dY^T X, or C += dY^T X for an fp32 C (dY T x N, X T x K, bf16)."""
+    T, N, lddy = _matrix(dy)
+    Tx, K, ldx = _matrix(x)
+    if Tx != T:
+        raise QsgError(f"token count mismatch: dY has {T}, X has {Tx}")
+    if _dtype_code(dy) != BF16 or _dtype_code(x) != BF16:
+        raise QsgError("qsg_wgrad_bf16 takes bf16 operands")
+    Nc, Kc, ldc = _matrix(c)
+    if (Nc, Kc) != (N, K):
+        raise QsgError(f"C is {Nc}x{Kc}, expected {N}x{K}")
+    _check(load_library().qsg_wgrad_bf16(_ptr(dy), T, N, lddy, _ptr(x), K, ldx, _ptr(c), _dtype_code(c), ldc,
+                                         1 if accumulate else 0, _stream(stream)))

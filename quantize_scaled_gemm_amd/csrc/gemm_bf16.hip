@@ -1,0 +1,186 @@
+// Weight-gradient GEMM in bf16 ("Low-Precision Training Guide", knob
+// --fp8-wgrad False: the wgrad GEMM stays in higher precision while fprop
+// and dgrad run in FP8):
+//
+//   C[n, k] (=, +=) sum_t dY[t, n] * X[t, k],   dY T x N, X T x K, bf16, row-major,
+//
+// fp32 accumulation, C N x K in bf16 (rounded to nearest even) or fp32 (the
+// fp32 main gradient, optionally accumulated: C = fp32(C + result)).
+//
+// Design for gfx950.  The contraction runs over the tokens t, the slow
+// dimension of both operands, so the kernel transposes on the way into LDS:
+//   * 128 x 128 output tile per workgroup of 256 threads (4 waves of 64 x 64,
+//     2 x 2 v_mfma_f32_32x32x16_bf16 each), 64 tokens per K step.
+//   * Threads 0-127 load dY, 128-255 load X: thread u holds the 8 x 8 block of
+//     tokens 8 (u % 8) .. +7 and features 8 (u / 8) .. +7 of the step's 64 x 128
+//     tile (eight 16-byte loads; the 64 lanes of a wave cover 8 token rows x
+//     128 contiguous bytes per load instruction).  The loads of step s + 1 are
+//     issued before the MFMAs of step s.
+//   * The 8 x 8 block is transposed in registers (32 v_perm_b32, pairs of
+//     16-bit halves) and written as 8 rows of 16 bytes into an LDS tile
+//     [feature][64 tokens] (128-byte rows); 16-byte chunk c of row f sits at
+//     position c ^ ((f >> 1) & 7), so a fragment read (16 lanes, 16
+//     consecutive features, one chunk) touches all 64 banks once.
+//   * MFMA operands are then 16-byte LDS reads: lane l supplies feature
+//     l % 32 of its block and tokens 8 (l / 32) .. +7 of a 16-token MFMA step,
+//     for both operands (any consistent split of the 16 tokens between the
+//     lane halves gives the same dot products).
+// Tokens past T and features past N / K are read as zero; results outside C
+// are not stored.  Operands whose rows are not 16-byte aligned take an
+// element-wise load path.
+#include <hip/hip_runtime.h>
+
+#include "qsg_device.h"
+#include "qsg_internal.h"
+
+namespace qsg {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int WT = 128;    // output tile (features of dY x features of X)
+constexpr int BT = 64;     // tokens per K step
+constexpr int ROWB = BT * 2;  // bytes per LDS row (one feature, 64 tokens)
+
+struct Bf16Args {
+  const uint16_t* dy;
+  const uint16_t* x;
+  int64_t T, N, K, lddy, ldx, ldc;
+  void* c;
+  bool vec;         // 16-byte loads of both operands
+  bool out_bf16;
+  bool accumulate;  // fp32 C only
+};
+
+__device__ __forceinline__ int swz(int f, int chunk) { return chunk ^ ((f >> 1) & 7); }
+
+// 8 x 8 block of bf16 (rows = tokens, 16 bytes each) of operand p at token
+// t0, feature f0 (row-major, leading dimension ld); out-of-range -> 0.
+__device__ __forceinline__ void load_block(const uint16_t* p, int64_t ld, int64_t t0, int64_t f0, int64_t T,
+                                           int64_t F, bool vec, u32x4 (&r)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t t = t0 + i;
+    if (vec && t < T && f0 + 8 <= F) {
+      r[i] = ld_stream16(p + t * ld + f0);
+    } else {
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+      if (t < T) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (f0 + e < F) w[e >> 1] |= (uint32_t)p[t * ld + f0 + e] << (16 * (e & 1));
+      }
+      r[i] = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  }
+}
+
+// Transpose the 8 x 8 block (r[token] = 8 features) and store feature rows:
+// row (frow + j) gets the 8 tokens of feature j as chunk `chunk`.
+__device__ __forceinline__ void store_block_t(uint8_t* lds, int frow, int chunk, const u32x4 (&r)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;  // high / low halves of the pair
+    u32x4 o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) o[p] = __builtin_amdgcn_perm(r[2 * p + 1][j >> 1], r[2 * p][j >> 1], sel);
+    const int f = frow + j;
+    *reinterpret_cast<u32x4*>(lds + f * ROWB + swz(f, chunk) * 16) = o;
+  }
+}
+
+__global__ __launch_bounds__(256) void gemm_wgrad_bf16_kernel(Bf16Args g) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[WT * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[WT * ROWB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t n0 = (int64_t)blockIdx.y * WT, k0 = (int64_t)blockIdx.x * WT;
+  // loader role
+  const bool is_b = tid >= 128;
+  const int u = tid & 127, tg = u & 7, fg = u >> 3;
+  const uint16_t* src = is_b ? g.x : g.dy;
+  const int64_t ld = is_b ? g.ldx : g.lddy;
+  const int64_t F = is_b ? g.K : g.N;
+  const int64_t fbase = (is_b ? k0 : n0) + fg * 8;
+  uint8_t* lds_dst = is_b ? lds_b : lds_a;
+  // MFMA role: wave (wn, wk) owns features wn*64.. of dY and wk*64.. of X
+  const int wn = wave >> 1, wk = wave & 1;
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int64_t nsteps = (g.T + BT - 1) / BT;
+  u32x4 r[8];
+  if (nsteps > 0) load_block(src, ld, (int64_t)tg * 8, fbase, g.T, F, g.vec, r);
+  for (int64_t s = 0; s < nsteps; ++s) {
+    store_block_t(lds_dst, fg * 8, tg, r);
+    __syncthreads();
+    if (s + 1 < nsteps) load_block(src, ld, (s + 1) * BT + tg * 8, fbase, g.T, F, g.vec, r);
+#pragma unroll
+    for (int ks = 0; ks < BT / 16; ++ks) {
+      const int chunk = ks * 2 + (lane >> 5);
+      bf16x8 fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int f = wn * 64 + i * 32 + (lane & 31);
+        fa[i] = *reinterpret_cast<const bf16x8*>(lds_a + f * ROWB + swz(f, chunk) * 16);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int f = wk * 64 + j * 32 + (lane & 31);
+        fb[j] = *reinterpret_cast<const bf16x8*>(lds_b + f * ROWB + swz(f, chunk) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  // accumulator tile (i, j): lane l holds column k = l % 32 and rows
+  // n = 8 (v / 4) + 4 (l / 32) + v % 4 of its 32 x 32 block
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t k = k0 + wk * 64 + j * 32 + (lane & 31);
+      if (k >= g.K) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t n = n0 + wn * 64 + i * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
+        if (n >= g.N) continue;
+        const float val = acc[i][j][v];
+        if (g.out_bf16) {
+          reinterpret_cast<uint16_t*>(g.c)[n * g.ldc + k] = (uint16_t)(pack_bf16x2(val, 0.0f) & 0xFFFF);
+        } else {
+          float* cp = reinterpret_cast<float*>(g.c) + n * g.ldc + k;
+          *cp = g.accumulate ? *cp + val : val;
+        }
+      }
+    }
+}
+
+}  // namespace
+
+void launch_wgrad_bf16(const void* dy, int64_t T, int64_t N, int64_t lddy, const void* x, int64_t K, int64_t ldx,
+                       void* c, int c_dtype, int64_t ldc, bool accumulate, hipStream_t st) {
+  Bf16Args g{};
+  g.dy = reinterpret_cast<const uint16_t*>(dy);
+  g.x = reinterpret_cast<const uint16_t*>(x);
+  g.T = T; g.N = N; g.K = K; g.lddy = lddy; g.ldx = ldx; g.ldc = ldc; g.c = c;
+  g.vec = ((uintptr_t)dy % 16 == 0) && ((uintptr_t)x % 16 == 0) && (lddy % 8 == 0) && (ldx % 8 == 0);
+  g.out_bf16 = (c_dtype == 1);
+  g.accumulate = accumulate && c_dtype == 0;
+  const dim3 grid((unsigned)((K + WT - 1) / WT), (unsigned)((N + WT - 1) / WT));
+  hipLaunchKernelGGL(gemm_wgrad_bf16_kernel, grid, dim3(256), 0, st, g);
+}
+
+}  // namespace qsg

@@ -126,6 +126,25 @@ int qsg_act_fp8_store_bwd(const void* da, int64_t rows, int64_t cols, int64_t ld
   return check_launch(fn);
 }
 
+int qsg_wgrad_bf16(const void* dy, int64_t T, int64_t N, int64_t lddy, const void* x, int64_t K, int64_t ldx,
+                   void* c, int c_dtype, int64_t ldc, int accumulate, void* stream) {
+  const char* fn = "qsg_wgrad_bf16";
+  if (!valid_dtype(c_dtype)) return fail(QSG_ERR_ARG, "%s: bad output dtype", fn);
+  if (T < 0 || N < 0 || K < 0) return fail(QSG_ERR_ARG, "%s: negative shape", fn);
+  if (accumulate && c_dtype != QSG_F32) return fail(QSG_ERR_UNSUPPORTED, "%s: accumulation needs an fp32 C", fn);
+  if (N == 0 || K == 0) return QSG_OK;
+  if (!c) return fail(QSG_ERR_ARG, "%s: null C", fn);
+  if (ldc < K) return fail(QSG_ERR_ARG, "%s: ldc < K", fn);
+  if (!aligned(c, c_dtype == QSG_BF16 ? 2 : 4)) return fail(QSG_ERR_ALIGN, "%s: C not aligned to its element size", fn);
+  if (T > 0) {
+    if (!dy || !x) return fail(QSG_ERR_ARG, "%s: null operand", fn);
+    if (lddy < N || ldx < K) return fail(QSG_ERR_ARG, "%s: lddy < N or ldx < K", fn);
+    if (!aligned(dy, 2) || !aligned(x, 2)) return fail(QSG_ERR_ALIGN, "%s: operands not aligned to 2 bytes", fn);
+  }
+  qsg::launch_wgrad_bf16(dy, T, N, lddy, x, K, ldx, c, c_dtype, ldc, accumulate != 0, as_stream(stream));
+  return check_launch(fn);
+}
+
 int qsg_amax_update(float* history_dev, int64_t hist_len, int64_t step, const float* amax_dev,
                     int algo, int fmt, int margin, float* scale_dev, float* scale_inv_dev,
                     void* stream) {

@@ -40,6 +40,10 @@ void launch_act_fp8_store_fwd(const void* h, int64_t rows, int64_t cols, int64_t
                               void* a, uint8_t* q, float* amax_out, hipStream_t st);
 void launch_act_fp8_store_bwd(const void* da, int64_t rows, int64_t cols, int64_t ld, int fmt, const uint8_t* q,
                               const float* scale_inv, void* dh, hipStream_t st);
+// bf16 weight gradient C[N x K] (=, +=) dY^T X over T tokens (dY T x N, X T x K,
+// row-major bf16); accumulate for fp32 C only.
+void launch_wgrad_bf16(const void* dy, int64_t T, int64_t N, int64_t lddy, const void* x, int64_t K, int64_t ldx,
+                       void* c, int c_dtype, int64_t ldc, bool accumulate, hipStream_t st);
 void launch_scaled_gemm(const uint8_t* a, int fa, int ka, const void* sa, const uint8_t* b, int fb,
                         int kb, const void* sb, int64_t M, int64_t N, int64_t K, int64_t lda,
                         int64_t ldb, void* c, int c_dtype, int64_t ldc, bool accumulate, hipStream_t st);

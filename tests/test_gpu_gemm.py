@@ -462,3 +462,99 @@ def test_accumulate_k_zero_keeps_c(q):
     c = torch.full((64, 32), 5.0, device="cuda")
     q.qsg_scaled_gemm_accumulate(a, 0, 0, dscal(1.0), b, 0, 0, dscal(1.0), c)
     assert np.all(to_np(c) == 5.0)
+
+
+# ---------------------------------------------------------------------------
+# wgrad kept in bf16 (qsg_wgrad_bf16, --fp8-wgrad False)
+# ---------------------------------------------------------------------------
+def bf16_dev(a32):
+    """float32 values that are exact in bf16 -> bf16 tensor on the GPU."""
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a32, dtype=np.float32)).to(torch.bfloat16).cuda()
+
+
+@pytest.mark.parametrize("T,N,K", [(256, 256, 256), (100, 130, 250), (1, 8, 8), (513, 128, 384), (0, 64, 32)])
+def test_wgrad_bf16_integer_exact(q, T, N, K):
+    """Integer-valued tokens (exact in bf16, sums below 2^24): fp32 out exact,
+    bf16 out the correctly rounded exact value; N = 130 takes the
+    element-wise load path; T = 0 gives zeros."""
+    import torch
+
+    g = workloads.generator(62, T, N, K)
+    dy = g.integers(-15, 16, (T, N)).astype(np.float32)
+    x = g.integers(-15, 16, (T, K)).astype(np.float32)
+    exact = dy.astype(np.float64).T @ x.astype(np.float64)
+    c32 = torch.full((N, K), float("nan"), device="cuda")
+    q.qsg_wgrad_bf16(bf16_dev(dy), bf16_dev(x), c32)
+    assert np.array_equal(to_np(c32).astype(np.float64), exact)
+    c16 = torch.full((N, K), float("nan"), device="cuda", dtype=torch.bfloat16)
+    q.qsg_wgrad_bf16(bf16_dev(dy), bf16_dev(x), c16)
+    assert np.array_equal(to_np(c16).astype(np.float64), f32_to_bf16_rne_f64(exact))
+
+
+@pytest.mark.parametrize("T,N,K", [(2048, 384, 512), (1000, 300, 200)])
+def test_wgrad_bf16_random_and_accumulate(q, T, N, K):
+    """dY ~ N(0, 1e-3), X ~ N(0, 1) bf16: bf16 and fp32 outputs within the
+    acceptance rule; two micro-batches accumulated into an fp32 C."""
+    import torch
+
+    dyb = [workloads.normal([63, mb, 0], (T, N), 1e-3) for mb in range(2)]
+    xb = [workloads.normal([63, mb, 1], (T, K), 1.0) for mb in range(2)]
+    dyf = [bf16_bits_to_f32_np(b) for b in dyb]
+    xf = [bf16_bits_to_f32_np(b) for b in xb]
+    ref0 = oracle.wgrad_bf16(dyf[0], xf[0])
+    for out in (torch.bfloat16, torch.float32):
+        c = torch.empty((N, K), device="cuda", dtype=out)
+        q.qsg_wgrad_bf16(to_dev_bf16_bits(dyb[0]), to_dev_bf16_bits(xb[0]), c)
+        ok, info = oracle.tolerance_check(to_np(c), ref0)
+        assert ok, (out, info)
+    c0 = workloads.normal([63, 9], (N, K), 1e-2, "f32")
+    c = to_dev(c0)
+    ref = c0.astype(np.float64)
+    for mb in range(2):
+        q.qsg_wgrad_bf16(to_dev_bf16_bits(dyb[mb]), to_dev_bf16_bits(xb[mb]), c, accumulate=True)
+        got = to_np(c).astype(np.float64)
+        ref = oracle.accumulate(np.float32(ref), oracle.wgrad_bf16(dyf[mb], xf[mb]))
+        ok, info = oracle.tolerance_check(got, ref)
+        assert ok, (mb, info)
+        ref = got
+
+
+def test_wgrad_bf16_full_size_sampled(q):
+    """dW = dY^T X of the 4096-hidden Linear (32768 tokens, 4096 x 4096) in
+    bf16, a seeded 64 x 64 sample of outputs against fp64 dot products."""
+    import torch
+
+    T, N, K = 32768, 4096, 4096
+    dyb = workloads.normal([64, 0], (T, N), 1e-3)
+    xb = workloads.normal([64, 1], (T, K), 1.0)
+    c = torch.empty((N, K), device="cuda", dtype=torch.bfloat16)
+    q.qsg_wgrad_bf16(to_dev_bf16_bits(dyb), to_dev_bf16_bits(xb), c)
+    got = to_np(c).astype(np.float64)
+    assert np.all(np.isfinite(got))
+    g = workloads.generator(64)
+    rows = np.sort(g.choice(N, 64, replace=False))
+    cols = np.sort(g.choice(K, 64, replace=False))
+    ref = oracle.wgrad_bf16(bf16_bits_to_f32_np(dyb[:, rows]), bf16_bits_to_f32_np(xb[:, cols]))
+    ok, info = oracle.tolerance_check(got[np.ix_(rows, cols)], ref)
+    assert ok, info
+
+
+def test_wgrad_bf16_rejects_bf16_accumulation(q):
+    import torch
+
+    dy = torch.zeros((8, 8), dtype=torch.bfloat16, device="cuda")
+    c = torch.zeros((8, 8), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(q.QsgError):
+        q.qsg_wgrad_bf16(dy, dy, c, accumulate=True)
+
+
+def bf16_bits_to_f32_np(bits):
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def to_dev_bf16_bits(bits):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()

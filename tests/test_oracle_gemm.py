@@ -155,3 +155,28 @@ def test_accumulate_over_micro_batches_vs_fraction():
     bad = np.asarray(c0, dtype=np.float64) - oracle.gemm_per_tensor(qdy[0], "e5m2", sa, qx[0], "e4m3", sb)
     bad = oracle.accumulate(np.float32(bad), oracle.gemm_per_tensor(qdy[1], "e5m2", sa, qx[1], "e4m3", sb))
     assert not np.all(np.abs(bad - exact) <= bound)
+
+
+def test_wgrad_bf16_vs_token_loop_and_fp8_convention():
+    """The bf16 wgrad against an exact rational loop over the tokens, and
+    against the FP8 wgrad convention (A = dY^T, B = X^T, C = A B^T) on values
+    that both formats hold exactly; a transposed operand fails both."""
+    g = np.random.Generator(np.random.PCG64(37))
+    T, N, K = 9, 4, 6
+    dy = g.integers(-8, 9, (T, N)).astype(np.float32) * np.float32(0.25)
+    x = g.integers(-15, 16, (T, K)).astype(np.float32)
+    ref = oracle.wgrad_bf16(dy, x)
+    exact = [[sum(Fraction(float(dy[t, n])) * Fraction(float(x[t, k])) for t in range(T)) for k in range(K)]
+             for n in range(N)]
+    assert np.array_equal(ref, as_float(exact))
+    qa = oracle.encode(np.ascontiguousarray(dy.T), "e5m2")
+    qb = oracle.encode(np.ascontiguousarray(x.T), "e4m3")
+    assert np.array_equal(ref, oracle.gemm_per_tensor(qa, "e5m2", np.float32(1), qb, "e4m3", np.float32(1)))
+    # square operands: dY used without its transpose has the right shape but
+    # not the right value
+    sq_dy = g.integers(-8, 9, (5, 5)).astype(np.float32)
+    sq_x = g.integers(-8, 9, (5, 5)).astype(np.float32)
+    sq = [[sum(Fraction(float(sq_dy[t, n])) * Fraction(float(sq_x[t, k])) for t in range(5)) for k in range(5)]
+          for n in range(5)]
+    assert np.array_equal(oracle.wgrad_bf16(sq_dy, sq_x), as_float(sq))
+    assert not np.array_equal(np.asarray(sq_dy, np.float64) @ np.asarray(sq_x, np.float64), as_float(sq))

@@ -14,8 +14,9 @@
 //   * Threads 0-127 load dY, 128-255 load X: thread u holds the 8 x 8 block of
 //     tokens 8 (u % 8) .. +7 and features 8 (u / 8) .. +7 of the step's 64 x 128
 //     tile (eight 16-byte loads; the 64 lanes of a wave cover 8 token rows x
-//     128 contiguous bytes per load instruction).  The loads of step s + 1 are
-//     issued before the MFMAs of step s.
+//     128 contiguous bytes per load instruction).  Two blocks are in flight
+//     per thread: the loads of step s + 2 are issued before the MFMAs of
+//     step s.
 //   * The 8 x 8 block is transposed in registers (32 v_perm_b32, pairs of
 //     16-bit halves) and written as 8 rows of 16 bytes into an LDS tile
 //     [feature][64 tokens] (128-byte rows); 16-byte chunk c of row f sits at
@@ -91,7 +92,7 @@ __device__ __forceinline__ void store_block_t(uint8_t* lds, int frow, int chunk,
   }
 }
 
-__global__ __launch_bounds__(256) void gemm_wgrad_bf16_kernel(Bf16Args g) {
+__global__ __launch_bounds__(256, 2) void gemm_wgrad_bf16_kernel(Bf16Args g) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[WT * ROWB];
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[WT * ROWB];
 
@@ -117,12 +118,12 @@ __global__ __launch_bounds__(256) void gemm_wgrad_bf16_kernel(Bf16Args g) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int64_t nsteps = (g.T + BT - 1) / BT;
-  u32x4 r[8];
-  if (nsteps > 0) load_block(src, ld, (int64_t)tg * 8, fbase, g.T, F, g.vec, r);
-  for (int64_t s = 0; s < nsteps; ++s) {
+  // One K step: stage the held block in LDS, fetch the block two steps ahead
+  // into the same registers, multiply out of LDS.
+  auto step = [&](u32x4 (&r)[8], int64_t s) {
     store_block_t(lds_dst, fg * 8, tg, r);
     __syncthreads();
-    if (s + 1 < nsteps) load_block(src, ld, (s + 1) * BT + tg * 8, fbase, g.T, F, g.vec, r);
+    if (s + 2 < nsteps) load_block(src, ld, (s + 2) * BT + tg * 8, fbase, g.T, F, g.vec, r);
 #pragma unroll
     for (int ks = 0; ks < BT / 16; ++ks) {
       const int chunk = ks * 2 + (lane >> 5);
@@ -143,6 +144,14 @@ __global__ __launch_bounds__(256) void gemm_wgrad_bf16_kernel(Bf16Args g) {
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
     __syncthreads();
+  };
+  // two register blocks in flight: even steps use r0, odd steps r1
+  u32x4 r0[8], r1[8];
+  if (nsteps > 0) load_block(src, ld, (int64_t)tg * 8, fbase, g.T, F, g.vec, r0);
+  if (nsteps > 1) load_block(src, ld, BT + (int64_t)tg * 8, fbase, g.T, F, g.vec, r1);
+  for (int64_t s = 0; s < nsteps; s += 2) {
+    step(r0, s);
+    if (s + 1 < nsteps) step(r1, s + 1);
   }
 
   // accumulator tile (i, j): lane l holds column k = l % 32 and rows

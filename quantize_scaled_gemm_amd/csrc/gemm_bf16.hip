@@ -9,18 +9,20 @@
 //
 // Design for gfx950.  The contraction runs over the tokens t, the slow
 // dimension of both operands, so the kernel transposes on the way into LDS:
-//   * 128 x 128 output tile per workgroup of 256 threads (4 waves of 64 x 64,
-//     2 x 2 v_mfma_f32_32x32x16_bf16 each), 64 tokens per K step.
+//   * 256 x 256 output tile per workgroup of 256 threads (4 waves of 128 x 128,
+//     4 x 4 v_mfma_f32_32x32x16_bf16 each, 256 accumulators per lane), 32
+//     tokens per K step: every 32-cycle MFMA needs 0.5 KB of fragment reads,
+//     so fragment reads and the transposed writes fit in the LDS bandwidth.
 //   * Threads 0-127 load dY, 128-255 load X: thread u holds the 8 x 8 block of
-//     tokens 8 (u % 8) .. +7 and features 8 (u / 8) .. +7 of the step's 64 x 128
-//     tile (eight 16-byte loads; the 64 lanes of a wave cover 8 token rows x
-//     128 contiguous bytes per load instruction).  Two blocks are in flight
+//     tokens 8 (u % 4) .. +7 and features 8 (u / 4) .. +7 of the step's 32 x 256
+//     tile (eight 16-byte loads; the 64 lanes of a wave cover 4 token rows x
+//     256 contiguous bytes per load instruction).  Two blocks are in flight
 //     per thread: the loads of step s + 2 are issued before the MFMAs of
 //     step s.
 //   * The 8 x 8 block is transposed in registers (32 v_perm_b32, pairs of
 //     16-bit halves) and written as 8 rows of 16 bytes into an LDS tile
-//     [feature][64 tokens] (128-byte rows); 16-byte chunk c of row f sits at
-//     position c ^ ((f >> 1) & 7), so a fragment read (16 lanes, 16
+//     [feature][32 tokens] (64-byte rows); 16-byte chunk c of row f sits at
+//     position c ^ ((f >> 2) & 3), so a fragment read (16 lanes, 16
 //     consecutive features, one chunk) touches all 64 banks once.
 //   * MFMA operands are then 16-byte LDS reads: lane l supplies feature
 //     l % 32 of its block and tokens 8 (l / 32) .. +7 of a 16-token MFMA step,
@@ -30,6 +32,8 @@
 // are not stored.  Operands whose rows are not 16-byte aligned take an
 // element-wise load path.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "qsg_device.h"
 #include "qsg_internal.h"
@@ -41,9 +45,9 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int WT = 128;    // output tile (features of dY x features of X)
-constexpr int BT = 64;     // tokens per K step
-constexpr int ROWB = BT * 2;  // bytes per LDS row (one feature, 64 tokens)
+constexpr int WT = 256;    // output tile (features of dY x features of X)
+constexpr int BT = 32;     // tokens per K step
+constexpr int ROWB = BT * 2;  // bytes per LDS row (one feature, 32 tokens: 4 chunks of 16 bytes)
 
 struct Bf16Args {
   const uint16_t* dy;
@@ -55,7 +59,9 @@ struct Bf16Args {
   bool accumulate;  // fp32 C only
 };
 
-__device__ __forceinline__ int swz(int f, int chunk) { return chunk ^ ((f >> 1) & 7); }
+// chunk c of row f at position c ^ ((f >> 2) & 3): 16 lanes reading one chunk
+// of 16 consecutive rows (64-byte rows: 4 rows per 64 banks) hit every bank once
+__device__ __forceinline__ int swz(int f, int chunk) { return chunk ^ ((f >> 2) & 3); }
 
 // 8 x 8 block of bf16 (rows = tokens, 16 bytes each) of operand p at token
 // t0, feature f0 (row-major, leading dimension ld); out-of-range -> 0.
@@ -92,81 +98,103 @@ __device__ __forceinline__ void store_block_t(uint8_t* lds, int frow, int chunk,
   }
 }
 
-__global__ __launch_bounds__(256, 2) void gemm_wgrad_bf16_kernel(Bf16Args g) {
+__global__ __launch_bounds__(256, 1) void gemm_wgrad_bf16_kernel(Bf16Args g) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[WT * ROWB];
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[WT * ROWB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n0 = (int64_t)blockIdx.y * WT, k0 = (int64_t)blockIdx.x * WT;
-  // loader role
+  // loader role: one 8-token x 8-feature block per step (tokens 8 tg.., features 8 fg..)
   const bool is_b = tid >= 128;
-  const int u = tid & 127, tg = u & 7, fg = u >> 3;
+  const int u = tid & 127, tg = u & 3, fg = u >> 2;
   const uint16_t* src = is_b ? g.x : g.dy;
   const int64_t ld = is_b ? g.ldx : g.lddy;
   const int64_t F = is_b ? g.K : g.N;
   const int64_t fbase = (is_b ? k0 : n0) + fg * 8;
   uint8_t* lds_dst = is_b ? lds_b : lds_a;
-  // MFMA role: wave (wn, wk) owns features wn*64.. of dY and wk*64.. of X
+  // MFMA role: wave (wn, wk) owns features wn*128.. of dY and wk*128.. of X
   const int wn = wave >> 1, wk = wave & 1;
 
-  v16f acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
   const int64_t nsteps = (g.T + BT - 1) / BT;
+  v16f acc[4][4];
   // One K step: stage the held block in LDS, fetch the block two steps ahead
-  // into the same registers, multiply out of LDS.
-  auto step = [&](u32x4 (&r)[8], int64_t s) {
+  // into the same registers, multiply out of LDS.  FIRST: the first MFMA of
+  // each accumulator tile starts from C = 0 (the accumulators get their first
+  // values from MFMAs, not from zero constants merged in at a loop head, which
+  // would make the register allocator copy them through VGPRs).
+  auto step = [&](u32x4 (&r)[8], int64_t s, auto first) {
     store_block_t(lds_dst, fg * 8, tg, r);
     __syncthreads();
     if (s + 2 < nsteps) load_block(src, ld, (s + 2) * BT + tg * 8, fbase, g.T, F, g.vec, r);
 #pragma unroll
     for (int ks = 0; ks < BT / 16; ++ks) {
       const int chunk = ks * 2 + (lane >> 5);
-      bf16x8 fa[2], fb[2];
+      bf16x8 fa[4], fb[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int f = wn * 64 + i * 32 + (lane & 31);
+      for (int i = 0; i < 4; ++i) {
+        const int f = wn * 128 + i * 32 + (lane & 31);
         fa[i] = *reinterpret_cast<const bf16x8*>(lds_a + f * ROWB + swz(f, chunk) * 16);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int f = wk * 64 + j * 32 + (lane & 31);
+      for (int j = 0; j < 4; ++j) {
+        const int f = wk * 128 + j * 32 + (lane & 31);
         fb[j] = *reinterpret_cast<const bf16x8*>(lds_b + f * ROWB + swz(f, chunk) * 16);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          if (decltype(first)::value && ks == 0) {
+            const v16f z = {};
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], z, 0, 0, 0);
+          } else {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          }
+        }
     }
     __syncthreads();
   };
+  if (nsteps == 0) {
+    // no tokens: the result is +0 (written, or added to the fp32 C)
+    for (int e = tid; e < WT * WT; e += 256) {
+      const int64_t n = n0 + e / WT, k = k0 + e % WT;
+      if (n >= g.N || k >= g.K) continue;
+      if (g.out_bf16) {
+        reinterpret_cast<uint16_t*>(g.c)[n * g.ldc + k] = 0;
+      } else {
+        float* cp = reinterpret_cast<float*>(g.c) + n * g.ldc + k;
+        *cp = g.accumulate ? *cp + 0.0f : 0.0f;
+      }
+    }
+    return;
+  }
   // two register blocks in flight: even steps use r0, odd steps r1
   u32x4 r0[8], r1[8];
-  if (nsteps > 0) load_block(src, ld, (int64_t)tg * 8, fbase, g.T, F, g.vec, r0);
+  load_block(src, ld, (int64_t)tg * 8, fbase, g.T, F, g.vec, r0);
   if (nsteps > 1) load_block(src, ld, BT + (int64_t)tg * 8, fbase, g.T, F, g.vec, r1);
-  for (int64_t s = 0; s < nsteps; s += 2) {
-    step(r0, s);
-    if (s + 1 < nsteps) step(r1, s + 1);
+  step(r0, 0, std::true_type{});
+  int64_t s = 1;
+  while (s < nsteps) {
+    step(r1, s, std::false_type{});
+    if (++s >= nsteps) break;
+    step(r0, s, std::false_type{});
+    ++s;
   }
 
   // accumulator tile (i, j): lane l holds column k = l % 32 and rows
   // n = 8 (v / 4) + 4 (l / 32) + v % 4 of its 32 x 32 block
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t k = k0 + wk * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < 4; ++j) {
+      const int64_t k = k0 + wk * 128 + j * 32 + (lane & 31);
       if (k >= g.K) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t n = n0 + wn * 64 + i * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
+        const int64_t n = n0 + wn * 128 + i * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
         if (n >= g.N) continue;
-        const float val = acc[i][j][v];
+        float val;
+        asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(val) : "a"(acc[i][j][v]));
         if (g.out_bf16) {
           reinterpret_cast<uint16_t*>(g.c)[n * g.ldc + k] = (uint16_t)(pack_bf16x2(val, 0.0f) & 0xFFFF);
         } else {

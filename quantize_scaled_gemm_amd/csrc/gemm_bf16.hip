@@ -17,8 +17,9 @@
 //     tokens 8 (u % 4) .. +7 and features 8 (u / 4) .. +7 of the step's 32 x 256
 //     tile (eight 16-byte loads; the 64 lanes of a wave cover 4 token rows x
 //     256 contiguous bytes per load instruction).  Two blocks are in flight
-//     per thread: the loads of step s + 2 are issued before the MFMAs of
-//     step s.
+//     per thread, and two LDS stages: while the MFMAs of step s run, the
+//     block of step s + 1 is transposed into the other stage and the block
+//     of step s + 2 fetched; one barrier per step.
 //   * The 8 x 8 block is transposed in registers (32 v_perm_b32, pairs of
 //     16-bit halves) and written as 8 rows of 16 bytes into an LDS tile
 //     [feature][32 tokens] (64-byte rows); 16-byte chunk c of row f sits at
@@ -99,8 +100,10 @@ __device__ __forceinline__ void store_block_t(uint8_t* lds, int frow, int chunk,
 }
 
 __global__ __launch_bounds__(256, 1) void gemm_wgrad_bf16_kernel(Bf16Args g) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[WT * ROWB];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[WT * ROWB];
+  // two stages: step s writes stage s & 1 while slower waves may still read
+  // the other, so one barrier per step suffices
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][WT * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][WT * ROWB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n0 = (int64_t)blockIdx.y * WT, k0 = (int64_t)blockIdx.x * WT;
@@ -111,21 +114,24 @@ __global__ __launch_bounds__(256, 1) void gemm_wgrad_bf16_kernel(Bf16Args g) {
   const int64_t ld = is_b ? g.ldx : g.lddy;
   const int64_t F = is_b ? g.K : g.N;
   const int64_t fbase = (is_b ? k0 : n0) + fg * 8;
-  uint8_t* lds_dst = is_b ? lds_b : lds_a;
   // MFMA role: wave (wn, wk) owns features wn*128.. of dY and wk*128.. of X
   const int wn = wave >> 1, wk = wave & 1;
 
   const int64_t nsteps = (g.T + BT - 1) / BT;
   v16f acc[4][4];
-  // One K step: stage the held block in LDS, fetch the block two steps ahead
-  // into the same registers, multiply out of LDS.  FIRST: the first MFMA of
-  // each accumulator tile starts from C = 0 (the accumulators get their first
-  // values from MFMAs, not from zero constants merged in at a loop head, which
-  // would make the register allocator copy them through VGPRs).
-  auto step = [&](u32x4 (&r)[8], int64_t s, auto first) {
-    store_block_t(lds_dst, fg * 8, tg, r);
-    __syncthreads();
-    if (s + 2 < nsteps) load_block(src, ld, (s + 2) * BT + tg * 8, fbase, g.T, F, g.vec, r);
+  // One K step s, on the block already in LDS stage s & 1: the block of step
+  // s + 1 (registers RN) is transposed into the other stage and the block of
+  // step s + 2 fetched into the registers RF (those of step s, stored one step
+  // earlier) while the MFMAs of step s run; then one barrier.  A stage is
+  // rewritten two steps after it was read, behind that barrier.  FIRST: the
+  // first MFMA of each accumulator tile starts from C = 0 (the accumulators
+  // get their first values from MFMAs, not from zero constants merged in at a
+  // loop head, which would make the register allocator copy them through
+  // VGPRs).
+  auto step = [&](u32x4 (&RN)[8], u32x4 (&RF)[8], int64_t s, auto first, auto stage) {
+    constexpr int ST = decltype(stage)::value;
+    if (s + 1 < nsteps) store_block_t(is_b ? lds_b[ST ^ 1] : lds_a[ST ^ 1], fg * 8, tg, RN);
+    if (s + 2 < nsteps) load_block(src, ld, (s + 2) * BT + tg * 8, fbase, g.T, F, g.vec, RF);
 #pragma unroll
     for (int ks = 0; ks < BT / 16; ++ks) {
       const int chunk = ks * 2 + (lane >> 5);
@@ -133,12 +139,12 @@ __global__ __launch_bounds__(256, 1) void gemm_wgrad_bf16_kernel(Bf16Args g) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int f = wn * 128 + i * 32 + (lane & 31);
-        fa[i] = *reinterpret_cast<const bf16x8*>(lds_a + f * ROWB + swz(f, chunk) * 16);
+        fa[i] = *reinterpret_cast<const bf16x8*>(lds_a[ST] + f * ROWB + swz(f, chunk) * 16);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int f = wk * 128 + j * 32 + (lane & 31);
-        fb[j] = *reinterpret_cast<const bf16x8*>(lds_b + f * ROWB + swz(f, chunk) * 16);
+        fb[j] = *reinterpret_cast<const bf16x8*>(lds_b[ST] + f * ROWB + swz(f, chunk) * 16);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -168,16 +174,20 @@ __global__ __launch_bounds__(256, 1) void gemm_wgrad_bf16_kernel(Bf16Args g) {
     }
     return;
   }
-  // two register blocks in flight: even steps use r0, odd steps r1
+  // two register blocks in flight: even steps' blocks in r0, odd steps' in r1
   u32x4 r0[8], r1[8];
   load_block(src, ld, (int64_t)tg * 8, fbase, g.T, F, g.vec, r0);
   if (nsteps > 1) load_block(src, ld, BT + (int64_t)tg * 8, fbase, g.T, F, g.vec, r1);
-  step(r0, 0, std::true_type{});
+  store_block_t(is_b ? lds_b[0] : lds_a[0], fg * 8, tg, r0);
+  __syncthreads();
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  step(r1, r0, 0, std::true_type{}, S0{});
   int64_t s = 1;
   while (s < nsteps) {
-    step(r1, s, std::false_type{});
+    step(r0, r1, s, std::false_type{}, S1{});
     if (++s >= nsteps) break;
-    step(r0, s, std::false_type{});
+    step(r1, r0, s, std::false_type{}, S0{});
     ++s;
   }
 

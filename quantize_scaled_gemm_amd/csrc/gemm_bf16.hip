@@ -10,20 +10,21 @@
 // Design for gfx950.  The contraction runs over the tokens t, the slow
 // dimension of both operands, so the kernel transposes on the way into LDS:
 //   * 256 x 256 output tile per workgroup of 256 threads (4 waves of 128 x 128,
-//     4 x 4 v_mfma_f32_32x32x16_bf16 each, 256 accumulators per lane), 32
+//     4 x 4 v_mfma_f32_32x32x16_bf16 each, 256 accumulators per lane), 64
 //     tokens per K step: every 32-cycle MFMA needs 0.5 KB of fragment reads,
 //     so fragment reads and the transposed writes fit in the LDS bandwidth.
-//   * Threads 0-127 load dY, 128-255 load X: thread u holds the 8 x 8 block of
-//     tokens 8 (u % 4) .. +7 and features 8 (u / 4) .. +7 of the step's 32 x 256
-//     tile (eight 16-byte loads; the 64 lanes of a wave cover 4 token rows x
-//     256 contiguous bytes per load instruction).  Two blocks are in flight
+//   * Threads 0-127 load dY, 128-255 load X: thread u holds the 8 x 8 blocks of
+//     tokens 8 (u % 4) .. +7 and 8 (u % 4 + 4) .. +7 and features
+//     8 (u / 4) .. +7 of the step's 64 x 256 tile (sixteen 16-byte loads; the
+//     64 lanes of a wave cover 4 token rows x 256 contiguous bytes per load
+//     instruction).  Two blocks are in flight
 //     per thread, and two LDS stages: while the MFMAs of step s run, the
 //     block of step s + 1 is transposed into the other stage and the block
 //     of step s + 2 fetched; one barrier per step.
 //   * The 8 x 8 block is transposed in registers (32 v_perm_b32, pairs of
 //     16-bit halves) and written as 8 rows of 16 bytes into an LDS tile
-//     [feature][32 tokens] (64-byte rows); 16-byte chunk c of row f sits at
-//     position c ^ ((f >> 2) & 3), so a fragment read (16 lanes, 16
+//     [feature][64 tokens] (128-byte rows); 16-byte chunk c of row f sits at
+//     position c ^ ((f >> 1) & 7), so a fragment read (16 lanes, 16
 //     consecutive features, one chunk) touches all 64 banks once.
 //   * MFMA operands are then 16-byte LDS reads: lane l supplies feature
 //     l % 32 of its block and tokens 8 (l / 32) .. +7 of a 16-token MFMA step,
@@ -47,8 +48,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int WT = 256;    // output tile (features of dY x features of X)
-constexpr int BT = 32;     // tokens per K step
-constexpr int ROWB = BT * 2;  // bytes per LDS row (one feature, 32 tokens: 4 chunks of 16 bytes)
+constexpr int BT = 64;     // tokens per K step
+constexpr int ROWB = BT * 2;  // bytes per LDS row (one feature, 64 tokens: 8 chunks of 16 bytes)
 
 struct Bf16Args {
   const uint16_t* dy;
@@ -60,9 +61,9 @@ struct Bf16Args {
   bool accumulate;  // fp32 C only
 };
 
-// chunk c of row f at position c ^ ((f >> 2) & 3): 16 lanes reading one chunk
-// of 16 consecutive rows (64-byte rows: 4 rows per 64 banks) hit every bank once
-__device__ __forceinline__ int swz(int f, int chunk) { return chunk ^ ((f >> 2) & 3); }
+// chunk c of row f at position c ^ ((f >> 1) & 7): 16 lanes reading one chunk
+// of 16 consecutive rows (128-byte rows: 2 rows per 64 banks) hit every bank once
+__device__ __forceinline__ int swz(int f, int chunk) { return chunk ^ ((f >> 1) & 7); }
 
 // 8 x 8 block of bf16 (rows = tokens, 16 bytes each) of operand p at token
 // t0, feature f0 (row-major, leading dimension ld); out-of-range -> 0.
@@ -107,7 +108,8 @@ __global__ __launch_bounds__(256, 1) void gemm_wgrad_bf16_kernel(Bf16Args g) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n0 = (int64_t)blockIdx.y * WT, k0 = (int64_t)blockIdx.x * WT;
-  // loader role: one 8-token x 8-feature block per step (tokens 8 tg.., features 8 fg..)
+  // loader role: two 8-token x 8-feature blocks per step (tokens 8 tg.. and
+  // 8 (tg + 4).., features 8 fg..)
   const bool is_b = tid >= 128;
   const int u = tid & 127, tg = u & 3, fg = u >> 2;
   const uint16_t* src = is_b ? g.x : g.dy;
@@ -128,10 +130,16 @@ __global__ __launch_bounds__(256, 1) void gemm_wgrad_bf16_kernel(Bf16Args g) {
   // get their first values from MFMAs, not from zero constants merged in at a
   // loop head, which would make the register allocator copy them through
   // VGPRs).
-  auto step = [&](u32x4 (&RN)[8], u32x4 (&RF)[8], int64_t s, auto first, auto stage) {
+  auto step = [&](u32x4 (&RN)[2][8], u32x4 (&RF)[2][8], int64_t s, auto first, auto stage) {
     constexpr int ST = decltype(stage)::value;
-    if (s + 1 < nsteps) store_block_t(is_b ? lds_b[ST ^ 1] : lds_a[ST ^ 1], fg * 8, tg, RN);
-    if (s + 2 < nsteps) load_block(src, ld, (s + 2) * BT + tg * 8, fbase, g.T, F, g.vec, RF);
+    if (s + 1 < nsteps) {
+      store_block_t(is_b ? lds_b[ST ^ 1] : lds_a[ST ^ 1], fg * 8, tg, RN[0]);
+      store_block_t(is_b ? lds_b[ST ^ 1] : lds_a[ST ^ 1], fg * 8, tg + 4, RN[1]);
+    }
+    if (s + 2 < nsteps) {
+      load_block(src, ld, (s + 2) * BT + tg * 8, fbase, g.T, F, g.vec, RF[0]);
+      load_block(src, ld, (s + 2) * BT + (tg + 4) * 8, fbase, g.T, F, g.vec, RF[1]);
+    }
 #pragma unroll
     for (int ks = 0; ks < BT / 16; ++ks) {
       const int chunk = ks * 2 + (lane >> 5);
@@ -175,10 +183,15 @@ __global__ __launch_bounds__(256, 1) void gemm_wgrad_bf16_kernel(Bf16Args g) {
     return;
   }
   // two register blocks in flight: even steps' blocks in r0, odd steps' in r1
-  u32x4 r0[8], r1[8];
-  load_block(src, ld, (int64_t)tg * 8, fbase, g.T, F, g.vec, r0);
-  if (nsteps > 1) load_block(src, ld, BT + (int64_t)tg * 8, fbase, g.T, F, g.vec, r1);
-  store_block_t(is_b ? lds_b[0] : lds_a[0], fg * 8, tg, r0);
+  u32x4 r0[2][8], r1[2][8];
+  load_block(src, ld, (int64_t)tg * 8, fbase, g.T, F, g.vec, r0[0]);
+  load_block(src, ld, (int64_t)(tg + 4) * 8, fbase, g.T, F, g.vec, r0[1]);
+  if (nsteps > 1) {
+    load_block(src, ld, BT + (int64_t)tg * 8, fbase, g.T, F, g.vec, r1[0]);
+    load_block(src, ld, BT + (int64_t)(tg + 4) * 8, fbase, g.T, F, g.vec, r1[1]);
+  }
+  store_block_t(is_b ? lds_b[0] : lds_a[0], fg * 8, tg, r0[0]);
+  store_block_t(is_b ? lds_b[0] : lds_a[0], fg * 8, tg + 4, r0[1]);
   __syncthreads();
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;

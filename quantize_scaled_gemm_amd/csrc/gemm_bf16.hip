@@ -228,6 +228,204 @@ __global__ __launch_bounds__(256, 1) void gemm_wgrad_bf16_kernel(Bf16Args g) {
     }
 }
 
+// ---- Aligned operands: global -> LDS directly, LDS transpose reads ----
+//
+// When both operands have 16-byte aligned rows and N, K are multiples of 8,
+// the tiles go into LDS as they lie in memory (buffer_load_dwordx4 ... lds)
+// and gfx950's LDS transpose read (ds_read_b64_tr_b16) forms the MFMA
+// operands, so no VGPRs stage the loads and nothing is transposed in
+// registers:
+//   * 32 tokens per step, a ring of 4 LDS stages of 32 x 256 per operand
+//     (512-byte token rows, 128 KB in all); the loads of step s + 3 are
+//     issued while the MFMAs of step s run, and a counted vmcnt wait plus a
+//     barrier at the end of step s makes step s + 1 visible.
+//   * Each wave issues 8 loads per step (4 per operand), each filling a
+//     1 KB block (2 token rows) of a stage; lane L fills position L % 32 of
+//     row L / 32, i.e. it fetches chunk (L % 32) ^ (4 (t % 4)) of token t.
+//   * Edges without branches: a step's buffer resource covers only the
+//     step's token rows that exist (none past the last step), and a lane
+//     whose 8 features lie past N / K gets an offset past the resource; both
+//     read as zero.
+//   * One ds_read_b64_tr_b16 transposes 4 x 4 blocks of 16-bit values within
+//     each 16-lane group: lane 4 e + q supplies 4 features of token e, and
+//     lane 4 q + r receives feature r of tokens 0..3.  Two such reads, 4
+//     token rows apart, give lane l tokens 8 (l / 32) .. +7 of feature l % 32
+//     of a 32-feature block: the operand layout of the 32x32x16 MFMA.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int DT = 32;                // tokens per step
+constexpr int DROWB = WT * 2;         // bytes per LDS row (one token, 256 features)
+constexpr int DOP = DT * DROWB;       // bytes per operand per stage
+constexpr int DLOADS = DOP / 1024 / 4;  // 1 KB loads per wave per operand per step
+constexpr uint32_t OUT_OF_RANGE = 0x80000000u;  // past any step's resource (< 2^31 bytes)
+
+// chunk c of token row t at position c ^ (4 (t % 4)): the 4 consecutive
+// token rows x 4 chunks that 32 lanes of a transpose read touch land on 16
+// different 16-byte bank groups
+__device__ __forceinline__ int tswz(int t, int chunk) { return chunk ^ ((t & 3) << 2); }
+
+// Byte offset, within an operand's stage, of what lane `lane` supplies to the
+// transpose reads of features fblk .. fblk + 31, tokens 0 .. 15: lane
+// 16 g + 4 e + q reads token 8 (g / 2) + e, features fblk + 16 (g % 2) + 4 q
+// .. + 3 (and, 4 rows further, token 8 (g / 2) + 4 + e).
+__device__ __forceinline__ int tr_offset(int fblk, int lane) {
+  const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+  const int t = 8 * (g >> 1) + e;
+  const int c = (fblk >> 3) + 2 * (g & 1) + (q >> 1);
+  return t * DROWB + tswz(t, c) * 16 + (q & 1) * 8;
+}
+
+__device__ __forceinline__ bf16x8 tr_frag(const uint8_t* p) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * DROWB));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Resource over the token rows of step `step` that exist, starting at
+// feature f0 of operand p.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t step_rsrc(const uint16_t* p, int64_t ld, int64_t f0, int64_t T,
+                                                            int64_t step) {
+  int64_t rows = T - step * DT;
+  rows = rows < 0 ? 0 : (rows > DT ? DT : rows);
+  const uint16_t* b = p + step * DT * ld + f0;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)b, 0, (int)(rows * ld * 2), 0x00020000);
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier without a memory fence (a fence would also wait for the
+// global -> LDS loads in flight); the waits it needs are explicit.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(256, 1) void gemm_wgrad_bf16_dma_kernel(Bf16Args g) {
+  // four distinct stage objects, so that reads of one stage need no wait for
+  // the loads in flight into the others; [0, DOP) dY, [DOP, 2 DOP) X
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * DOP];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[2 * DOP];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[2 * DOP];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[2 * DOP];
+
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t n0 = (int64_t)blockIdx.y * WT, k0 = (int64_t)blockIdx.x * WT;
+
+  // load j of an operand fills 1 KB block (j * 4 + wave) of its stage: token
+  // rows 2 (j * 4 + wave) + L / 32, position L % 32
+  uint32_t voa[DLOADS], vob[DLOADS];
+#pragma unroll
+  for (int j = 0; j < DLOADS; ++j) {
+    const int t = 2 * (j * 4 + wave) + (lane >> 5);
+    const int c = tswz(t, lane & 31);
+    voa[j] = n0 + 8 * c < g.N ? (uint32_t)((t * g.lddy + 8 * c) * 2) : OUT_OF_RANGE;
+    vob[j] = k0 + 8 * c < g.K ? (uint32_t)((t * g.ldx + 8 * c) * 2) : OUT_OF_RANGE;
+  }
+  const int wn = wave >> 1, wk = wave & 1;
+  int offa[4], offb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    offa[i] = tr_offset(wn * 128 + i * 32, lane);
+    offb[i] = DOP + tr_offset(wk * 128 + i * 32, lane);
+  }
+
+  const int64_t nsteps = (g.T + DT - 1) / DT;
+  // the loads of step `step` into stage object `dst`
+  auto issue = [&](uint8_t* dst, int64_t step) {
+    const __amdgpu_buffer_rsrc_t ra = step_rsrc(g.dy, g.lddy, n0, g.T, step);
+    const __amdgpu_buffer_rsrc_t rb = step_rsrc(g.x, g.ldx, k0, g.T, step);
+#pragma unroll
+    for (int j = 0; j < DLOADS; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(dst + (j * 4 + wave) * 1024), 16, voa[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < DLOADS; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(dst + DOP + (j * 4 + wave) * 1024), 16, vob[j], 0,
+                                               0, 0);
+  };
+
+  v16f acc[4][4];
+  // Step s on stage `cur`: the loads of step s + 3 go into `next3` (the
+  // stage of step s - 1, which every wave left before the last barrier), the
+  // MFMAs run on `cur`, then the wait for step s + 1's loads (at most the 2
+  // younger steps' 2 DLOADS loads each are still in flight) and a barrier.
+  // FIRST: the first MFMA of each accumulator tile starts from C = 0.
+  auto step = [&](const uint8_t* cur, uint8_t* next3, int64_t s, auto first) {
+    issue(next3, s + 3);
+#pragma unroll
+    for (int ks = 0; ks < DT / 16; ++ks) {
+      bf16x8 fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = tr_frag(cur + ks * 16 * DROWB + offa[i]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[j] = tr_frag(cur + ks * 16 * DROWB + offb[j]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (decltype(first)::value && ks == 0) {
+            const v16f z = {};
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], z, 0, 0, 0);
+          } else {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          }
+        }
+    }
+    wait_vm<4 * DLOADS>();
+    lds_barrier();
+  };
+
+  issue(st0, 0);
+  issue(st1, 1);
+  issue(st2, 2);
+  wait_vm<4 * DLOADS>();
+  lds_barrier();
+  step(st0, st3, 0, std::true_type{});
+  int64_t s = 1;
+  while (true) {
+    if (s >= nsteps) break;
+    step(st1, st0, s++, std::false_type{});
+    if (s >= nsteps) break;
+    step(st2, st1, s++, std::false_type{});
+    if (s >= nsteps) break;
+    step(st3, st2, s++, std::false_type{});
+    if (s >= nsteps) break;
+    step(st0, st3, s++, std::false_type{});
+  }
+  wait_vm<0>();  // the loads past the last step (empty resources) have landed
+
+  // accumulator tile (i, j): lane l holds column k = l % 32 and rows
+  // n = 8 (v / 4) + 4 (l / 32) + v % 4 of its 32 x 32 block
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t k = k0 + wk * 128 + j * 32 + (lane & 31);
+      if (k >= g.K) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t n = n0 + wn * 128 + i * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
+        if (n >= g.N) continue;
+        float val;
+        asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(val) : "a"(acc[i][j][v]));
+        if (g.out_bf16) {
+          reinterpret_cast<uint16_t*>(g.c)[n * g.ldc + k] = (uint16_t)(pack_bf16x2(val, 0.0f) & 0xFFFF);
+        } else {
+          float* cp = reinterpret_cast<float*>(g.c) + n * g.ldc + k;
+          *cp = g.accumulate ? *cp + val : val;
+        }
+      }
+    }
+}
+
 }  // namespace
 
 void launch_wgrad_bf16(const void* dy, int64_t T, int64_t N, int64_t lddy, const void* x, int64_t K, int64_t ldx,
@@ -240,7 +438,13 @@ void launch_wgrad_bf16(const void* dy, int64_t T, int64_t N, int64_t lddy, const
   g.out_bf16 = (c_dtype == 1);
   g.accumulate = accumulate && c_dtype == 0;
   const dim3 grid((unsigned)((K + WT - 1) / WT), (unsigned)((N + WT - 1) / WT));
-  hipLaunchKernelGGL(gemm_wgrad_bf16_kernel, grid, dim3(256), 0, st, g);
+  // direct-to-LDS path: aligned rows, whole 16-byte chunks at the feature
+  // edges, and a step's rows (32 x ld x 2 bytes) within a 31-bit resource
+  const bool dma = g.vec && N % 8 == 0 && K % 8 == 0 && lddy < (1 << 24) && ldx < (1 << 24) && T > 0;
+  if (dma)
+    hipLaunchKernelGGL(gemm_wgrad_bf16_dma_kernel, grid, dim3(256), 0, st, g);
+  else
+    hipLaunchKernelGGL(gemm_wgrad_bf16_kernel, grid, dim3(256), 0, st, g);
 }
 
 }  // namespace qsg

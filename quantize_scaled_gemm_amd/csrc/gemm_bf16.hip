@@ -390,16 +390,17 @@ __global__ __launch_bounds__(256, 1) void gemm_wgrad_bf16_dma_kernel(Bf16Args g)
   lds_barrier();
   step(st0, st3, 0, std::true_type{});
   int64_t s = 1;
-  while (true) {
-    if (s >= nsteps) break;
-    step(st1, st0, s++, std::false_type{});
-    if (s >= nsteps) break;
-    step(st2, st1, s++, std::false_type{});
-    if (s >= nsteps) break;
-    step(st3, st2, s++, std::false_type{});
-    if (s >= nsteps) break;
-    step(st0, st3, s++, std::false_type{});
+  // whole groups of 4 steps in the loop, the rest after it (a loop with
+  // exits between its steps makes the compiler drain every load at its head)
+  for (; s + 4 <= nsteps; s += 4) {
+    step(st1, st0, s, std::false_type{});
+    step(st2, st1, s + 1, std::false_type{});
+    step(st3, st2, s + 2, std::false_type{});
+    step(st0, st3, s + 3, std::false_type{});
   }
+  if (s < nsteps) step(st1, st0, s++, std::false_type{});
+  if (s < nsteps) step(st2, st1, s++, std::false_type{});
+  if (s < nsteps) step(st3, st2, s++, std::false_type{});
   wait_vm<0>();  // the loads past the last step (empty resources) have landed
 
   // accumulator tile (i, j): lane l holds column k = l % 32 and rows

@@ -309,6 +309,22 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Output tile of workgroup b (1-D grid of nx * ny).  Workgroups go to the 8
+// XCDs round-robin (b % 8), each XCD with its own L2, so XCD j is given the
+// j-th eighth of a tile order that walks groups of 4 tile rows column by
+// column: the 32 tiles an XCD runs at once on a 16 x 16 grid span 4 dY and
+// 8 X panels (12 panels, instead of 18 in row-major order).
+__device__ __forceinline__ void tile_of(int b, int nx, int ny, int& tx, int& ty) {
+  constexpr int GH = 4;
+  const int total = nx * ny;
+  const int l = total % 8 == 0 ? (b % 8) * (total / 8) + b / 8 : b;
+  const int y0 = l / (GH * nx) * GH;
+  const int h = ny - y0 < GH ? ny - y0 : GH;
+  const int idx = l - y0 * nx;
+  ty = y0 + idx % h;
+  tx = idx / h;
+}
+
 __global__ __launch_bounds__(256, 1) void gemm_wgrad_bf16_dma_kernel(Bf16Args g) {
   // four distinct stage objects, so that reads of one stage need no wait for
   // the loads in flight into the others; [0, DOP) dY, [DOP, 2 DOP) X
@@ -318,7 +334,9 @@ __global__ __launch_bounds__(256, 1) void gemm_wgrad_bf16_dma_kernel(Bf16Args g)
   __shared__ __attribute__((aligned(1024))) uint8_t st3[2 * DOP];
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t n0 = (int64_t)blockIdx.y * WT, k0 = (int64_t)blockIdx.x * WT;
+  int tx, ty;
+  tile_of(blockIdx.x, (int)((g.K + WT - 1) / WT), (int)((g.N + WT - 1) / WT), tx, ty);
+  const int64_t n0 = (int64_t)ty * WT, k0 = (int64_t)tx * WT;
 
   // load j of an operand fills 1 KB block (j * 4 + wave) of its stage: token
   // rows 2 (j * 4 + wave) + L / 32, position L % 32
@@ -378,6 +396,13 @@ __global__ __launch_bounds__(256, 1) void gemm_wgrad_bf16_dma_kernel(Bf16Args g)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
           }
         }
+    }
+    // spread this step's fetches over its MFMAs (one per 3), rather than
+    // letting them issue as one burst that stalls the MFMA issue
+#pragma unroll
+    for (int q = 0; q < 2 * DLOADS; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
     }
     wait_vm<4 * DLOADS>();
     lds_barrier();
@@ -443,7 +468,7 @@ void launch_wgrad_bf16(const void* dy, int64_t T, int64_t N, int64_t lddy, const
   // edges, and a step's rows (32 x ld x 2 bytes) within a 31-bit resource
   const bool dma = g.vec && N % 8 == 0 && K % 8 == 0 && lddy < (1 << 24) && ldx < (1 << 24) && T > 0;
   if (dma)
-    hipLaunchKernelGGL(gemm_wgrad_bf16_dma_kernel, grid, dim3(256), 0, st, g);
+    hipLaunchKernelGGL(gemm_wgrad_bf16_dma_kernel, dim3(grid.x * grid.y), dim3(256), 0, st, g);
   else
     hipLaunchKernelGGL(gemm_wgrad_bf16_kernel, grid, dim3(256), 0, st, g);
 }

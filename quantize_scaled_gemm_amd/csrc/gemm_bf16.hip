@@ -7,8 +7,14 @@
 // fp32 accumulation, C N x K in bf16 (rounded to nearest even) or fp32 (the
 // fp32 main gradient, optionally accumulated: C = fp32(C + result)).
 //
-// Design for gfx950.  The contraction runs over the tokens t, the slow
-// dimension of both operands, so the kernel transposes on the way into LDS:
+// Two kernels.  Operands with 16-byte aligned rows and N, K multiples of 8
+// (every Linear layer's) take gemm_wgrad_bf16_dma_kernel further down: direct
+// global -> LDS loads and LDS transpose reads.  Any other shape or alignment
+// takes the general kernel below.
+//
+// General kernel, designed for gfx950.  The contraction runs over the tokens
+// t, the slow dimension of both operands, so the kernel transposes on the way
+// into LDS:
 //   * 256 x 256 output tile per workgroup of 256 threads (4 waves of 128 x 128,
 //     4 x 4 v_mfma_f32_32x32x16_bf16 each, 256 accumulators per lane), 64
 //     tokens per K step: every 32-cycle MFMA needs 0.5 KB of fragment reads,

@@ -199,8 +199,10 @@ int qsg_act_fp8_store_bwd(const void* da, int64_t rows, int64_t cols, int64_t ld
  *
  *   dy  T x N bf16 (tokens x output features), leading dimension lddy;
  *   x   T x K bf16 (tokens x input features), leading dimension ldx; both
- *       2-byte aligned (the vector path needs 16-byte aligned rows: bases
- *       16-byte aligned, lddy and ldx multiples of 8);
+ *       2-byte aligned.  The fast path needs 16-byte aligned rows (bases
+ *       16-byte aligned, lddy and ldx multiples of 8 and below 2^24) and N,
+ *       K multiples of 8; other operands take a slower general path with the
+ *       same results;
  *   c   N x K, ldc, c_dtype QSG_BF16 (rounded to nearest even) or QSG_F32,
  *       aligned to its element size; products of bf16 values are exact in
  *       fp32 and are summed in fp32.

@@ -475,13 +475,15 @@ def bf16_dev(a32):
 
 
 @pytest.mark.parametrize("T,N,K", [(256, 256, 256), (100, 130, 250), (1, 8, 8), (513, 128, 384), (0, 64, 32),
-                                   (777, 200, 264), (40, 512, 8)])
+                                   (777, 200, 264), (40, 512, 8), (96, 760, 2048), (64, 1264, 2048)])
 def test_wgrad_bf16_integer_exact(q, T, N, K):
     """Integer-valued tokens (exact in bf16, sums below 2^24): fp32 out exact,
     bf16 out the correctly rounded exact value; N = 130 takes the
     element-wise load path, the others with N, K multiples of 8 the direct
     global -> LDS path (777 x 200 x 264: ragged steps and partial tiles on
-    both feature edges); T = 0 gives zeros."""
+    both feature edges; 760 x 2048 and 1264 x 2048: 24 and 40 tiles, which
+    take the XCD tile order with a last group of 3 and of 1 tile rows);
+    T = 0 gives zeros."""
     import torch
 
     g = workloads.generator(62, T, N, K)

@@ -546,6 +546,29 @@ def test_wgrad_bf16_full_size_sampled(q):
     assert ok, info
 
 
+@pytest.mark.parametrize("offset", [0, 1])
+def test_wgrad_bf16_strided_operands(q, offset):
+    """Operands as views into wider buffers whose padding holds 7.0 (leading
+    dimensions N + 24 and K + 40): offset 0 keeps 16-byte aligned rows (the
+    direct-to-LDS path with ld > width), offset 1 shifts the bases by one
+    element (the general path).  Integer values: fp32 out exact, padding
+    never read."""
+    import torch
+
+    T, N, K = 300, 264, 520
+    g = workloads.generator(64, T, N, K, offset)
+    dy = g.integers(-15, 16, (T, N)).astype(np.float32)
+    x = g.integers(-15, 16, (T, K)).astype(np.float32)
+    dyw = torch.full((T, N + 24), 7.0, dtype=torch.bfloat16, device="cuda")
+    xw = torch.full((T, K + 40), 7.0, dtype=torch.bfloat16, device="cuda")
+    dyw[:, offset:offset + N] = bf16_dev(dy)
+    xw[:, offset:offset + K] = bf16_dev(x)
+    c = torch.full((N, K), float("nan"), device="cuda")
+    q.qsg_wgrad_bf16(dyw[:, offset:offset + N], xw[:, offset:offset + K], c)
+    exact = dy.astype(np.float64).T @ x.astype(np.float64)
+    assert np.array_equal(to_np(c).astype(np.float64), exact)
+
+
 def test_wgrad_bf16_rejects_bf16_accumulation(q):
     import torch
 

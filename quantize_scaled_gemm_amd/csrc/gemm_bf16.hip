@@ -435,6 +435,41 @@ __global__ __launch_bounds__(256, 1) void gemm_wgrad_bf16_dma_kernel(Bf16Args g)
   wait_vm<0>();  // the loads past the last step (empty resources) have landed
 
   // accumulator tile (i, j): lane l holds column k = l % 32 and rows
+  // n = 8 (v / 4) + 4 (l / 32) + v % 4 of its 32 x 32 block.  A wave's store
+  // of one v covers 32 consecutive columns of two rows.  Interior tiles take
+  // a branch-free path, so that the 16 reads of an fp32 C being accumulated
+  // are in flight together instead of one read-add-write at a time.
+  if (n0 + WT <= g.N && k0 + WT <= g.K) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t k = k0 + wk * 128 + j * 32 + (lane & 31);
+        const int64_t nb = n0 + wn * 128 + i * 32 + 4 * (lane >> 5);
+        float val[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(val[v]) : "a"(acc[i][j][v]));
+        if (g.out_bf16) {
+          uint16_t* cp = reinterpret_cast<uint16_t*>(g.c) + nb * g.ldc + k;
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            cp[(8 * (v / 4) + v % 4) * g.ldc] = (uint16_t)(pack_bf16x2(val[v], 0.0f) & 0xFFFF);
+        } else {
+          float* cp = reinterpret_cast<float*>(g.c) + nb * g.ldc + k;
+          if (g.accumulate) {
+            float old[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) old[v] = cp[(8 * (v / 4) + v % 4) * g.ldc];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) val[v] += old[v];
+          }
+#pragma unroll
+          for (int v = 0; v < 16; ++v) cp[(8 * (v / 4) + v % 4) * g.ldc] = val[v];
+        }
+      }
+    return;
+  }
+  // accumulator tile (i, j): lane l holds column k = l % 32 and rows
   // n = 8 (v / 4) + 4 (l / 32) + v % 4 of its 32 x 32 block
 #pragma unroll
   for (int i = 0; i < 4; ++i)

@@ -241,11 +241,11 @@ __global__ __launch_bounds__(256, 1) void gemm_wgrad_bf16_kernel(Bf16Args g) {
 // and gfx950's LDS transpose read (ds_read_b64_tr_b16) forms the MFMA
 // operands, so no VGPRs stage the loads and nothing is transposed in
 // registers:
-//   * 32 tokens per step, a ring of 4 LDS stages of 32 x 256 per operand
-//     (512-byte token rows, 128 KB in all); the loads of step s + 3 are
+//   * 48 tokens per step, a ring of 3 LDS stages of 48 x 256 per operand
+//     (512-byte token rows, 144 KB in all); the loads of step s + 2 are
 //     issued while the MFMAs of step s run, and a counted vmcnt wait plus a
 //     barrier at the end of step s makes step s + 1 visible.
-//   * Each wave issues 8 loads per step (4 per operand), each filling a
+//   * Each wave issues 12 loads per step (6 per operand), each filling a
 //     1 KB block (2 token rows) of a stage; lane L fills position L % 32 of
 //     row L / 32, i.e. it fetches chunk (L % 32) ^ (4 (t % 4)) of token t.
 //   * Edges without branches: a step's buffer resource covers only the
@@ -262,7 +262,7 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int DT = 32;                // tokens per step
+constexpr int DT = 48;                // tokens per step
 constexpr int DROWB = WT * 2;         // bytes per LDS row (one token, 256 features)
 constexpr int DOP = DT * DROWB;       // bytes per operand per stage
 constexpr int DLOADS = DOP / 1024 / 4;  // 1 KB loads per wave per operand per step
@@ -332,12 +332,11 @@ __device__ __forceinline__ void tile_of(int b, int nx, int ny, int& tx, int& ty)
 }
 
 __global__ __launch_bounds__(256, 1) void gemm_wgrad_bf16_dma_kernel(Bf16Args g) {
-  // four distinct stage objects, so that reads of one stage need no wait for
+  // three distinct stage objects, so that reads of one stage need no wait for
   // the loads in flight into the others; [0, DOP) dY, [DOP, 2 DOP) X
   __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * DOP];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[2 * DOP];
   __shared__ __attribute__((aligned(1024))) uint8_t st2[2 * DOP];
-  __shared__ __attribute__((aligned(1024))) uint8_t st3[2 * DOP];
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int tx, ty;
@@ -377,13 +376,13 @@ __global__ __launch_bounds__(256, 1) void gemm_wgrad_bf16_dma_kernel(Bf16Args g)
   };
 
   v16f acc[4][4];
-  // Step s on stage `cur`: the loads of step s + 3 go into `next3` (the
+  // Step s on stage `cur`: the loads of step s + 2 go into `next2` (the
   // stage of step s - 1, which every wave left before the last barrier), the
-  // MFMAs run on `cur`, then the wait for step s + 1's loads (at most the 2
-  // younger steps' 2 DLOADS loads each are still in flight) and a barrier.
+  // MFMAs run on `cur`, then the wait for step s + 1's loads (at most the
+  // younger step's 2 DLOADS loads are still in flight) and a barrier.
   // FIRST: the first MFMA of each accumulator tile starts from C = 0.
-  auto step = [&](const uint8_t* cur, uint8_t* next3, int64_t s, auto first) {
-    issue(next3, s + 3);
+  auto step = [&](const uint8_t* cur, uint8_t* next2, int64_t s, auto first) {
+    issue(next2, s + 2);
 #pragma unroll
     for (int ks = 0; ks < DT / 16; ++ks) {
       bf16x8 fa[4], fb[4];
@@ -410,28 +409,25 @@ __global__ __launch_bounds__(256, 1) void gemm_wgrad_bf16_dma_kernel(Bf16Args g)
       __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
     }
-    wait_vm<4 * DLOADS>();
+    wait_vm<2 * DLOADS>();
     lds_barrier();
   };
 
   issue(st0, 0);
   issue(st1, 1);
-  issue(st2, 2);
-  wait_vm<4 * DLOADS>();
+  wait_vm<2 * DLOADS>();
   lds_barrier();
-  step(st0, st3, 0, std::true_type{});
+  step(st0, st2, 0, std::true_type{});
   int64_t s = 1;
-  // whole groups of 4 steps in the loop, the rest after it (a loop with
+  // whole groups of 3 steps in the loop, the rest after it (a loop with
   // exits between its steps makes the compiler drain every load at its head)
-  for (; s + 4 <= nsteps; s += 4) {
+  for (; s + 3 <= nsteps; s += 3) {
     step(st1, st0, s, std::false_type{});
     step(st2, st1, s + 1, std::false_type{});
-    step(st3, st2, s + 2, std::false_type{});
-    step(st0, st3, s + 3, std::false_type{});
+    step(st0, st2, s + 2, std::false_type{});
   }
   if (s < nsteps) step(st1, st0, s++, std::false_type{});
   if (s < nsteps) step(st2, st1, s++, std::false_type{});
-  if (s < nsteps) step(st3, st2, s++, std::false_type{});
   wait_vm<0>();  // the loads past the last step (empty resources) have landed
 
   // accumulator tile (i, j): lane l holds column k = l % 32 and rows

@@ -502,7 +502,7 @@ void launch_wgrad_bf16(const void* dy, int64_t T, int64_t N, int64_t lddy, const
   g.accumulate = accumulate && c_dtype == 0;
   const dim3 grid((unsigned)((K + WT - 1) / WT), (unsigned)((N + WT - 1) / WT));
   // direct-to-LDS path: aligned rows, whole 16-byte chunks at the feature
-  // edges, a step's rows (32 x ld x 2 bytes) within a 31-bit resource, and the
+  // edges, a step's rows (48 x ld x 2 bytes) within a 31-bit resource, and the
   // tiles within a 1-D grid
   const bool dma = g.vec && N % 8 == 0 && K % 8 == 0 && lddy < (1 << 24) && ldx < (1 << 24) && T > 0 &&
                    (uint64_t)grid.x * grid.y <= 0x7FFFFFFFu;

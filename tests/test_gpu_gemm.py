@@ -526,19 +526,23 @@ def test_wgrad_bf16_random_and_accumulate(q, T, N, K):
         ref = got
 
 
-def test_wgrad_bf16_full_size_sampled(q):
-    """dW = dY^T X of the 4096-hidden Linear (32768 tokens, 4096 x 4096) in
-    bf16, a seeded 64 x 64 sample of outputs against fp64 dot products."""
+@pytest.mark.parametrize("N,K", [(4096, 4096), (14336, 4096), (4096, 14336)])
+def test_wgrad_bf16_full_size_sampled(q, N, K):
+    """dW = dY^T X of the 4096-hidden Linear's layers over 32768 tokens in bf16
+    (4096 x 4096; 14336 x 4096 and 4096 x 14336, the FFN layer's two weight
+    gradients: 896 tiles in the XCD order), a seeded 64 x 64 sample of outputs
+    against fp64 dot products."""
     import torch
 
-    T, N, K = 32768, 4096, 4096
-    dyb = workloads.normal([64, 0], (T, N), 1e-3)
-    xb = workloads.normal([64, 1], (T, K), 1.0)
+    T = 32768
+    key = [] if (N, K) == (4096, 4096) else [N, K]
+    dyb = workloads.normal([64, 0] + key, (T, N), 1e-3)
+    xb = workloads.normal([64, 1] + key, (T, K), 1.0)
     c = torch.empty((N, K), device="cuda", dtype=torch.bfloat16)
     q.qsg_wgrad_bf16(to_dev_bf16_bits(dyb), to_dev_bf16_bits(xb), c)
     got = to_np(c).astype(np.float64)
     assert np.all(np.isfinite(got))
-    g = workloads.generator(64)
+    g = workloads.generator(64, *key)
     rows = np.sort(g.choice(N, 64, replace=False))
     cols = np.sort(g.choice(K, 64, replace=False))
     ref = oracle.wgrad_bf16(bf16_bits_to_f32_np(dyb[:, rows]), bf16_bits_to_f32_np(xb[:, cols]))

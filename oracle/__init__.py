@@ -59,6 +59,8 @@ from .gemm import (  # noqa: F401
     accumulate,
     wgrad_bf16,
     tolerance_check,
+    mx_operand,
+    mfma_accumulation_bound,
 )
 from .activation import (  # noqa: F401
     gelu,

@@ -128,6 +128,46 @@ def _matrix(t):
     return rows, cols, max(ld, cols)
 
 
+def _buffer(t, name, numel, dtype, required=True):
+    """Check a buffer the library reads or writes densely: on the GPU,
+    contiguous, exactly ``numel`` elements of ``dtype`` ("u8", "f32", "bf16").
+    Raw integer pointers are passed through unchecked (the C ABI's own
+    contract applies to them)."""
+    if t is None:
+        if required:
+            raise QsgError(f"{name} is required")
+        return
+    if isinstance(t, int):
+        return
+    import torch
+
+    want = {"u8": torch.uint8, "f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    if not t.is_cuda:
+        raise QsgError(f"{name} must live on the GPU")
+    if t.dtype != want:
+        raise QsgError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.numel() != numel:
+        raise QsgError(f"{name} must hold exactly {numel} elements (got {t.numel()}, shape {tuple(t.shape)})")
+    if numel > 0 and not t.is_contiguous():
+        raise QsgError(f"{name} must be contiguous")
+
+
+def _scale_layout(kind, rows, K):
+    """(numel, dtype) of a scale tensor of the given kind for an operand of
+    `rows` rows and contraction length K (include/qsg.h, qsg_scaling), or
+    None when K breaks the kind's block rule (the library then reports the
+    shape error)."""
+    if kind in (TENSORWISE, DELAYED):
+        return 1, "f32"
+    if kind == MXFP8:
+        return (rows * (K // 32), "u8") if K % 32 == 0 else None
+    if kind == BLOCK_1X128:
+        return (rows * (K // 128), "f32") if K % 128 == 0 else None
+    if kind == BLOCK_128X128:
+        return (((rows + 127) // 128) * (K // 128), "f32") if K % 128 == 0 else None
+    return None
+
+
 def _stream(stream):
     if stream is not None:
         return stream if isinstance(stream, int) else stream.cuda_stream
@@ -153,21 +193,31 @@ def qsg_version():
 def qsg_amax(x, amax, stream=None):
     """amax (1 fp32 on the GPU) = max |x|."""
     rows, cols, ld = _matrix(x)
+    _buffer(amax, "amax", 1, "f32")
     _check(load_library().qsg_amax(_ptr(x), _dtype_code(x), rows, cols, ld, _ptr(amax), _stream(stream)))
 
 
 def qsg_compute_scale(amax, fmt, margin, scale, scale_inv, stream=None):
+    for t, n in ((amax, "amax"), (scale, "scale"), (scale_inv, "scale_inv")):
+        _buffer(t, n, 1, "f32")
     _check(load_library().qsg_compute_scale(_ptr(amax), fmt, margin, _ptr(scale), _ptr(scale_inv),
                                             _stream(stream)))
 
 
 def qsg_cast_transpose(x, fmt, scale, q=None, qt=None, amax_out=None, stream=None):
     rows, cols, ld = _matrix(x)
+    _buffer(scale, "scale", 1, "f32")
+    _buffer(q, "q", rows * cols, "u8", required=False)
+    _buffer(qt, "qt", rows * cols, "u8", required=False)
+    _buffer(amax_out, "amax_out", 1, "f32", required=False)
     _check(load_library().qsg_cast_transpose(_ptr(x), _dtype_code(x), rows, cols, ld, fmt, _ptr(scale),
                                              _ptr(q), _ptr(qt), _ptr(amax_out), _stream(stream)))
 
 
 def qsg_amax_update(history, step, amax, fmt, margin, scale, scale_inv, algo=AMAX_MAX, stream=None):
+    _buffer(history, "history", history.numel(), "f32")
+    for t, n in ((amax, "amax"), (scale, "scale"), (scale_inv, "scale_inv")):
+        _buffer(t, n, 1, "f32")
     _check(load_library().qsg_amax_update(_ptr(history), history.numel(), step, _ptr(amax), algo, fmt,
                                           margin, _ptr(scale), _ptr(scale_inv), _stream(stream)))
 
@@ -175,9 +225,41 @@ def qsg_amax_update(history, step, amax, fmt, margin, scale, scale_inv, algo=AMA
 def qsg_quantize(x, scaling, fmt, q=None, s=None, qt=None, st=None, margin=0, mx_rule=MX_CEIL,
                  stream=None):
     rows, cols, ld = _matrix(x)
+    _buffer(q, "q", rows * cols, "u8", required=False)
+    _buffer(qt, "qt", rows * cols, "u8", required=False)
+    if scaling == TENSORWISE:
+        _buffer(s, "s", 3, "f32")
+    elif scaling in (MXFP8, BLOCK_1X128, BLOCK_128X128):
+        # row-wise copy: blocks along cols; column-wise copy: blocks along rows
+        if scaling == BLOCK_128X128:
+            ok = rows % 128 == 0 and cols % 128 == 0
+            row = col = ((rows // 128) * (cols // 128), "f32") if ok else None
+        else:
+            row, col = _scale_layout(scaling, rows, cols), _scale_layout(scaling, cols, rows)
+        if row is not None and q is not None:
+            _buffer(s, "s", row[0], row[1])
+        if col is not None and qt is not None:
+            _buffer(st, "st", col[0], col[1])
     rec = Recipe(scaling, fmt, margin, mx_rule)
     _check(load_library().qsg_quantize(_ptr(x), _dtype_code(x), rows, cols, ld, ctypes.byref(rec),
                                        _ptr(q), _ptr(s), _ptr(qt), _ptr(st), _stream(stream)))
+
+
+def _gemm_operands(a, b):
+    import torch
+
+    for t, name in ((a, "A"), (b, "B")):
+        if t.dtype != torch.uint8:
+            raise QsgError(f"{name} must hold FP8 bytes as uint8 (got {t.dtype})")
+        if not t.is_cuda:
+            raise QsgError(f"{name} must live on the GPU")
+
+
+def _gemm_scales(ka, sa, M, kb, sb, N, K):
+    for kind, t, rows, name in ((ka, sa, M, "sa"), (kb, sb, N, "sb")):
+        lay = _scale_layout(kind, rows, K)
+        if lay is not None:
+            _buffer(t, name, lay[0], lay[1])
 
 
 def qsg_scaled_gemm(a, fa, ka, sa, b, fb, kb, sb, c, stream=None):
@@ -189,6 +271,8 @@ def qsg_scaled_gemm(a, fa, ka, sa, b, fb, kb, sb, c, stream=None):
     Mc, Nc, ldc = _matrix(c)
     if (Mc, Nc) != (M, N):
         raise QsgError(f"C is {Mc}x{Nc}, expected {M}x{N}")
+    _gemm_operands(a, b)
+    _gemm_scales(ka, sa, M, kb, sb, N, K)
     _check(load_library().qsg_scaled_gemm(_ptr(a), fa, ka, _ptr(sa), _ptr(b), fb, kb, _ptr(sb), M, N, K,
                                           lda, ldb, _ptr(c), _dtype_code(c), ldc, _stream(stream)))
 
@@ -206,6 +290,8 @@ def qsg_scaled_gemm_accumulate(a, fa, ka, sa, b, fb, kb, sb, c, stream=None):
         raise QsgError(f"C is {Mc}x{Nc}, expected {M}x{N}")
     if c.dtype != torch.float32:
         raise QsgError("qsg_scaled_gemm_accumulate accumulates into an fp32 C")
+    _gemm_operands(a, b)
+    _gemm_scales(ka, sa, M, kb, sb, N, K)
     _check(load_library().qsg_scaled_gemm_accumulate(_ptr(a), fa, ka, _ptr(sa), _ptr(b), fb, kb, _ptr(sb), M, N,
                                                      K, lda, ldb, _ptr(c), ldc, _stream(stream)))
 
@@ -215,6 +301,10 @@ def qsg_act_fp8_store_fwd(h, fmt, scale, a, q, amax_out=None, stream=None):
     rows, cols, ld = _matrix(h)
     if _dtype_code(h) != BF16:
         raise QsgError("qsg_act_fp8_store_fwd takes a bf16 input")
+    _buffer(scale, "scale", 1, "f32")
+    _buffer(a, "a", rows * cols, "bf16")
+    _buffer(q, "q", rows * cols, "u8")
+    _buffer(amax_out, "amax_out", 1, "f32", required=False)
     _check(load_library().qsg_act_fp8_store_fwd(_ptr(h), rows, cols, ld, fmt, _ptr(scale), _ptr(a), _ptr(q),
                                                 _ptr(amax_out), _stream(stream)))
 
@@ -224,6 +314,9 @@ def qsg_act_fp8_store_bwd(da, fmt, q, scale_inv, dh, stream=None):
     rows, cols, ld = _matrix(da)
     if _dtype_code(da) != BF16:
         raise QsgError("qsg_act_fp8_store_bwd takes a bf16 gradient")
+    _buffer(q, "q", rows * cols, "u8")
+    _buffer(scale_inv, "scale_inv", 1, "f32")
+    _buffer(dh, "dh", rows * cols, "bf16")
     _check(load_library().qsg_act_fp8_store_bwd(_ptr(da), rows, cols, ld, fmt, _ptr(q), _ptr(scale_inv), _ptr(dh),
                                                 _stream(stream)))
 

@@ -3,8 +3,9 @@
 tensorwise hybrid), in the launch configuration bench.py times.
 
 Quantized bytes and scales are compared in full (bit-exact).  GEMM outputs
-are compared on a seeded sample of output elements, each computed by the
-oracle as an fp64 dot product of the dequantized row and column.
+are compared on a seeded sample of 256 output rows x 256 output columns,
+each element computed by the oracle as an fp64 dot product of the
+dequantized row and column.
 """
 
 import numpy as np
@@ -89,8 +90,8 @@ def test_fullsize_gemm_sampled(q, linear, gname):
     q.qsg_scaled_gemm(qa, A["code"], q.TENSORWISE, A["s"][2:3], qb, B["code"], q.TENSORWISE, B["s"][2:3], c)
     torch.cuda.synchronize()
     g = workloads.generator(50, len(gname))
-    rows = np.sort(g.choice(Mo, 64, replace=False))
-    cols = np.sort(g.choice(No, 64, replace=False))
+    rows = np.sort(g.choice(Mo, 256, replace=False))
+    cols = np.sort(g.choice(No, 256, replace=False))
     ra = qa[torch.from_numpy(rows).cuda()].cpu().numpy()
     rb = qb[torch.from_numpy(cols).cuda()].cpu().numpy()
     sai = A["s"][2].item()

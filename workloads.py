@@ -23,7 +23,8 @@ Workloads (shapes and distributions of the FP8 Linear configurations):
                    dY_t 8192x4096 ~N(0,1e-3); 64 steps
   mxfp8_4096       X 16384x4096, W 14336x4096 ~N(0,0.02); dY 16384x14336
                    ~N(0,1e-3)
-  blockwise_7168   X 16384x7168, W 18432x7168 Student-t (nu=3)
+  blockwise_7168   X 16384x7168, W 18432x7168 Student-t (nu=3); dY
+                   16384x18432 Student-t (nu=3) x 1e-3 for the backward GEMMs
   linear_4096      X 32768x4096 ~N(0,1); W 4096x4096 and W2 14336x4096
                    ~N(0,0.02); dY 32768x4096 and dY2 32768x14336 ~N(0,1e-3)
 """
@@ -86,8 +87,8 @@ def normal(key, shape, std=1.0, dtype="bf16"):
     return _draw(key, shape, lambda g, s: g.standard_normal(s, dtype=np.float32), std, dtype)
 
 
-def student_t(key, shape, nu=3.0, dtype="bf16"):
-    return _draw(key, shape, lambda g, s: g.standard_t(nu, s), 1.0, dtype)
+def student_t(key, shape, nu=3.0, dtype="bf16", scale=1.0):
+    return _draw(key, shape, lambda g, s: g.standard_t(nu, s), scale, dtype)
 
 
 def with_outlier_channels(x_bits, key, frac=0.01, factor=50.0):
@@ -134,9 +135,14 @@ def mxfp8_4096(m=16384, n=14336, k=4096, with_dy=True):
     return out
 
 
-def blockwise_7168(m=16384, n=18432, k=7168):
+def blockwise_7168(m=16384, n=18432, k=7168, with_dy=False):
+    """X and W; with_dy adds the output gradient dY [m x n] that the backward
+    GEMMs (dgrad, wgrad) consume, Student-t (nu=3) times 1e-3."""
     w = WORKLOAD_IDS["blockwise_7168"]
-    return {"X": student_t([w, 0], (m, k)), "W": student_t([w, 1], (n, k))}
+    out = {"X": student_t([w, 0], (m, k)), "W": student_t([w, 1], (n, k))}
+    if with_dy:
+        out["dY"] = student_t([w, 2], (m, n), scale=1e-3)
+    return out
 
 
 def linear_4096(m=32768, h=4096, f=14336, which=("X", "W", "W2", "dY", "dY2")):

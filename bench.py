@@ -272,8 +272,8 @@ def workload_tensorwise_256(torch, q, dev, cold):
 
 def workload_delayed_4096(torch, q, dev, cold):
     """delayed_4096: one step of delayed scaling (history 1024, max, margin 0)
-    for X, W (E4M3) and dY (E5M2): cast + transpose with fused amax, history
-    update, then fprop, dgrad and wgrad 8192 x 4096 x 4096."""
+    for X, W (E4M3) and dY (E5M2): cast + transpose, amax and history update
+    in one launch per tensor, then fprop, dgrad and wgrad 8192 x 4096 x 4096."""
     import workloads
 
     st = workloads.delayed_4096_step(1)
@@ -287,17 +287,22 @@ def workload_delayed_4096(torch, q, dev, cold):
                     amax=torch.zeros(1, device=dev), scale=torch.ones(1, device=dev),
                     sinv=torch.ones(1, device=dev), hist=torch.zeros(1024, device=dev))
     out = {}
-    for n in ("X", "dY"):
+    ws = torch.zeros(q.DELAYED_WORKSPACE_BYTES // 4, dtype=torch.int32, device=dev)
+    for n in ("X", "W", "dY"):
+        # one launch: cast + transpose with the scale in force, amax, history
+        # update and the next scale
         t = b[n]
         r, c = t["x"].shape
-        out[f"cast_amax_{n}"] = entry(4.0 * r * c, cold.time(
-            lambda t=t: q.qsg_cast_transpose(t["x"], t["f"], t["scale"], t["q"], t["qt"], t["amax"])), "hbm")
+        out[f"step_{n}"] = entry(4.0 * r * c, cold.time(
+            lambda t=t: q.qsg_cast_transpose_delayed(t["x"], t["f"], 0, t["hist"], 1, t["scale"], t["sinv"],
+                                                     t["q"], t["qt"], t["amax"], ws)), "hbm")
+    # the same step as two calls (cast + transpose with fused amax, then the
+    # history update): three launches
     t = b["X"]
-    out["amax_update"] = entry(0.0, cold.time(
-        lambda: q.qsg_amax_update(t["hist"], 1, t["amax"], t["f"], 0, t["scale"], t["sinv"])), "hbm")
-    for n in ("W",):
-        t = b[n]
-        q.qsg_cast_transpose(t["x"], t["f"], t["scale"], t["q"], t["qt"], t["amax"])
+    r, c = t["x"].shape
+    out["step_X_two_calls"] = entry(4.0 * r * c, cold.time(
+        lambda: (q.qsg_cast_transpose(t["x"], t["f"], t["scale"], t["q"], t["qt"], t["amax"]),
+                 q.qsg_amax_update(t["hist"], 1, t["amax"], t["f"], 0, t["scale"], t["sinv"]))), "hbm")
     x, w, dy = b["X"], b["W"], b["dY"]
     R, C = X.shape
     bf = dict(dtype=torch.bfloat16, device=dev)

@@ -161,6 +161,41 @@ int qsg_amax_update(float* history_dev, int64_t hist_len, int64_t step,
                     const float* amax_dev, int algo, int fmt, int margin,
                     float* scale_dev, float* scale_inv_dev, void* stream);
 
+/* Bytes of the workspace qsg_cast_transpose_delayed needs (33 lines of 128
+ * bytes: per-group maxima and arrival counts, and one common counter). */
+#define QSG_DELAYED_WORKSPACE_BYTES 4224
+
+/* One step of delayed scaling for one tensor, in a single kernel launch
+ * ("Low-Precision Training Guide", recipe "delayed": the tensor is quantized
+ * with the scale derived from earlier steps' amaxes, and its own amax enters a
+ * rolling history; knobs --fp8-amax-history-len, --fp8-amax-compute-algo max,
+ * --fp8-margin; "How to reduce cuda memory usage of fp8?": the transposed copy
+ * that backward reads).  The result is that of
+ *     qsg_cast_transpose(x, ..., fmt, scale_dev, q, qt, amax_out_dev)
+ *     qsg_amax_update(history_dev, hist_len, step, amax, QSG_AMAX_MAX, fmt,
+ *                     margin, scale_dev, scale_inv_dev)
+ * with the amax passed between the two kept in `workspace`:
+ *   x, dtype, rows, cols, ld, fmt, q, qt   as qsg_cast_transpose (q, qt may
+ *                 not both be NULL unless the tensor is empty); q and qt are
+ *                 written with the scale in force at entry.
+ *   margin        --fp8-margin, in [0, 64].
+ *   history_dev, hist_len, step, scale_dev, scale_inv_dev   as
+ *                 qsg_amax_update: on return *scale_dev / *scale_inv_dev hold
+ *                 the scale for the next step (unchanged when the window max
+ *                 is 0 or not finite).
+ *   amax_out_dev  out: 1 float, max |x| of this call (as qsg_amax), or NULL.
+ *   workspace     device memory of QSG_DELAYED_WORKSPACE_BYTES bytes, 4-byte
+ *                 aligned (128-byte alignment keeps each counter on its own
+ *                 cache line), owned by the caller, zero before its first use;
+ *                 every call leaves it zero again.  Calls that share one
+ *                 workspace must not overlap (same stream, or ordered).
+ * The last workgroup of the launch does the history update, so no second
+ * kernel and no host synchronisation is needed. */
+int qsg_cast_transpose_delayed(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt,
+                               int margin, float* history_dev, int64_t hist_len, int64_t step,
+                               float* scale_dev, float* scale_inv_dev, uint8_t* q, uint8_t* qt,
+                               float* amax_out_dev, void* workspace, void* stream);
+
 /* FP8 store of the MLP activation's input, forward ("Benefits of Using FP8
  * Precision with MegaDLMs and Required Hardware", configuration field
  * activation_func_fp8_input_store: the activation's input is kept in FP8 for

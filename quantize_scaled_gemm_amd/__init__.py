@@ -31,6 +31,7 @@ ENTRY_POINTS = (
     "qsg_amax",
     "qsg_compute_scale",
     "qsg_cast_transpose",
+    "qsg_cast_transpose_delayed",
     "qsg_amax_update",
     "qsg_quantize",
     "qsg_scaled_gemm",
@@ -74,6 +75,8 @@ def load_library(path=LIB_PATH):
     lib.qsg_compute_scale.argtypes = [F, I, I, F, F, P]
     lib.qsg_cast_transpose.restype = I
     lib.qsg_cast_transpose.argtypes = [P, I, I64, I64, I64, I, F, P, P, F, P]
+    lib.qsg_cast_transpose_delayed.restype = I
+    lib.qsg_cast_transpose_delayed.argtypes = [P, I, I64, I64, I64, I, I, F, I64, I64, F, F, P, P, F, P, P]
     lib.qsg_amax_update.restype = I
     lib.qsg_amax_update.argtypes = [F, I64, I64, F, I, I, I, F, F, P]
     lib.qsg_quantize.restype = I
@@ -212,6 +215,35 @@ def qsg_cast_transpose(x, fmt, scale, q=None, qt=None, amax_out=None, stream=Non
     _buffer(amax_out, "amax_out", 1, "f32", required=False)
     _check(load_library().qsg_cast_transpose(_ptr(x), _dtype_code(x), rows, cols, ld, fmt, _ptr(scale),
                                              _ptr(q), _ptr(qt), _ptr(amax_out), _stream(stream)))
+
+
+DELAYED_WORKSPACE_BYTES = 4224  # QSG_DELAYED_WORKSPACE_BYTES of include/qsg.h
+
+
+def qsg_cast_transpose_delayed(x, fmt, margin, history, step, scale, scale_inv, q=None, qt=None, amax_out=None,
+                               workspace=None, stream=None):
+    """One delayed-scaling step of x in one launch: q / qt with the scale in
+    force, amax into history[step mod len], scale / scale_inv for the next
+    step.  workspace: DELAYED_WORKSPACE_BYTES zeroed bytes on the GPU, reused
+    from call to call (every call leaves it zero)."""
+    rows, cols, ld = _matrix(x)
+    _buffer(history, "history", history.numel(), "f32")
+    for t, n in ((scale, "scale"), (scale_inv, "scale_inv")):
+        _buffer(t, n, 1, "f32")
+    _buffer(q, "q", rows * cols, "u8", required=False)
+    _buffer(qt, "qt", rows * cols, "u8", required=False)
+    _buffer(amax_out, "amax_out", 1, "f32", required=False)
+    if workspace is None:
+        raise QsgError("workspace is required")
+    if not isinstance(workspace, int):
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise QsgError("workspace must be a contiguous GPU tensor")
+        if workspace.numel() * workspace.element_size() < DELAYED_WORKSPACE_BYTES:
+            raise QsgError(f"workspace must hold at least {DELAYED_WORKSPACE_BYTES} bytes")
+    _check(load_library().qsg_cast_transpose_delayed(_ptr(x), _dtype_code(x), rows, cols, ld, fmt, margin,
+                                                     _ptr(history), history.numel(), step, _ptr(scale),
+                                                     _ptr(scale_inv), _ptr(q), _ptr(qt), _ptr(amax_out),
+                                                     _ptr(workspace), _stream(stream)))
 
 
 def qsg_amax_update(history, step, amax, fmt, margin, scale, scale_inv, algo=AMAX_MAX, stream=None):

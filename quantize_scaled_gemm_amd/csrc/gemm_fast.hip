@@ -244,16 +244,75 @@ __device__ __forceinline__ void mfma_range(v16f (&acc)[TMW][TN], const Frags<TN>
   }
 }
 
-// An accumulator element copied to a VGPR (keeps the accumulators in AGPRs
-// for the register allocator).
-__device__ __forceinline__ float acc_read(float a) {
-  float v;
-  asm("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
-  return v;
+// The 16 accumulators of one 32 x 32 tile copied to VGPRs (keeps the
+// accumulators in AGPRs for the register allocator).  The reads come as one
+// block into 16 distinct registers, so the multiplies that follow find their
+// inputs ready instead of each waiting for the read just before it.
+__device__ __forceinline__ void acc_read16(const v16f& a, float (&o)[16]) {
+#pragma unroll
+  for (int q = 0; q < 16; q += 4)
+    asm("v_accvgpr_read_b32 %0, %4\n\tv_accvgpr_read_b32 %1, %5\n\t"
+        "v_accvgpr_read_b32 %2, %6\n\tv_accvgpr_read_b32 %3, %7"
+        : "=v"(o[q]), "=v"(o[q + 1]), "=v"(o[q + 2]), "=v"(o[q + 3])
+        : "a"(a[q]), "a"(a[q + 1]), "a"(a[q + 2]), "a"(a[q + 3]));
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) uint8_t gbyte;
+
+// One 32 x 32 accumulator tile scaled by alpha and rearranged for 64-byte
+// row stores.  In the tile, lane l holds row l % 32 and, for group g = 0..3,
+// columns 8g + 4(l / 32) + 0..3.  For bf16 a swap between the lane halves
+// (v_permlane32_swap) of groups 2p and 2p + 1 gives every lane 8 consecutive
+// columns (16 bytes); fp32 groups are 16 bytes already.  A second swap
+// between lanes l and l + 16 (v_permlane16_swap) of two such pieces makes 4
+// lanes hold 64 contiguous bytes of one row: xs[pr] holds rows 0..15 and
+// ys[pr] rows 16..31 of the 64-byte column pair pr (bf16: one pair, fp32:
+// two).  All 16 reads come first, then all multiplies, then the conversions,
+// so each stage uses results issued several instructions earlier.
+template <bool OUT_BF16>
+__device__ __forceinline__ void tile_pieces(const v16f& acc, float alpha, u32x4 (&xs)[OUT_BF16 ? 1 : 2],
+                                            u32x4 (&ys)[OUT_BF16 ? 1 : 2]) {
+  float v[16];
+  acc_read16(acc, v);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] *= alpha;
+  constexpr int NPAIR = OUT_BF16 ? 1 : 2;
+  u32x4 lo[2], hi[2];  // per pair: the 16-byte pieces before the row swap
+  if constexpr (OUT_BF16) {
+    uint32_t pk[4][2];
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      pk[gq][0] = pack_bf16x2(v[gq * 4 + 0], v[gq * 4 + 1]);
+      pk[gq][1] = pack_bf16x2(v[gq * 4 + 2], v[gq * 4 + 3]);
+    }
+    // lane halves: lane l gets columns 8h .. 8h+7 (lo) and 16 + 8h .. (hi)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const auto s0 = __builtin_amdgcn_permlane32_swap(pk[2 * p][0], pk[2 * p + 1][0], false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(pk[2 * p][1], pk[2 * p + 1][1], false, false);
+      (p == 0 ? lo[0] : hi[0]) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+    }
+  } else {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const u32x4 w = {__float_as_uint(v[gq * 4 + 0]), __float_as_uint(v[gq * 4 + 1]),
+                       __float_as_uint(v[gq * 4 + 2]), __float_as_uint(v[gq * 4 + 3])};
+      ((gq & 1) ? hi[gq >> 1] : lo[gq >> 1]) = w;
+    }
+  }
+  // row swap: lanes 0-15 give their hi piece to lanes 16-31 for their lo
+  // piece (and 32-47 / 48-63 alike), so that x holds rows 0-15 and y rows 16-31
+#pragma unroll
+  for (int pr = 0; pr < NPAIR; ++pr) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const auto sw = __builtin_amdgcn_permlane16_swap(lo[pr][d], hi[pr][d], false, false);
+      xs[pr][d] = sw[0];
+      ys[pr][d] = sw[1];
+    }
+  }
+}
 
 // Tile t of the XCD-aware order: workgroup ids are dispatched round-robin
 // over the 8 XCDs, each XCD owns a contiguous range of the logical tile
@@ -414,14 +473,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     // (The last step's reads of f0 are repeated after it, so that the
     // fragments are not held through the epilogue.)
 
-    // ---- epilogue: scale, convert, store straight from registers ----
-    // In a 32 x 32 accumulator tile, lane l holds row l % 32 and, for group
-    // g = 0..3, columns 8g + 4(l / 32) + 0..3.  For bf16 a swap between the
-    // lane halves (v_permlane32_swap) of groups 2p and 2p + 1 gives every lane
-    // 8 consecutive columns (16 bytes); fp32 groups are 16 bytes already.  A
-    // second swap between lanes l and l + 16 (v_permlane16_swap) of two such
-    // pieces makes 4 lanes hold 64 contiguous bytes of one row, so every store
-    // writes 16 rows x 64 bytes.
+    // ---- epilogue: scale, convert, store straight from registers (see
+    // tile_pieces); every store writes 16 rows x 64 contiguous bytes ----
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
     // tile coordinates made opaque here, so that no address below is
     // computed ahead of the K loop and kept live across it
@@ -441,62 +494,49 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     const int r16 = elane & 15, pidx = eh + 2 * ((elane >> 4) & 1);
     const uint32_t loff = ((uint32_t)r16 * (uint32_t)ldc * ESZ) + (uint32_t)pidx * 16;
     constexpr int NPAIR = OUT_BF16 ? 1 : 2;  // 64-byte column pairs per 32 x 32 tile
+    if (interior) {
+      // every piece of the workgroup's tile is inside C: straight-line code
+      // with no per-tile branch, one scheduling region per accumulator tile
 #pragma unroll
-    for (int i = 0; i < TMW; ++i) {
+      for (int i = 0; i < TMW; ++i) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        u32x4 lo[2], hi[2];  // per pair: the 16-byte pieces before / after the row swap
-        if constexpr (OUT_BF16) {
-          uint32_t pk[4][2];
+        for (int j = 0; j < TN; ++j) {
+          u32x4 xs[NPAIR], ys[NPAIR];
+          tile_pieces<OUT_BF16>(acc[i][j], alpha, xs, ys);
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const float v0 = acc_read(acc[i][j][gq * 4 + 0]) * alpha, v1 = acc_read(acc[i][j][gq * 4 + 1]) * alpha;
-            const float v2 = acc_read(acc[i][j][gq * 4 + 2]) * alpha, v3 = acc_read(acc[i][j][gq * 4 + 3]) * alpha;
-            pk[gq][0] = pack_bf16x2(v0, v1);
-            pk[gq][1] = pack_bf16x2(v2, v3);
-          }
-          // lane halves: lane l gets columns 8h .. 8h+7 (lo) and 16 + 8h .. (hi)
+          for (int pr = 0; pr < NPAIR; ++pr) {
+            const int cb = j * 32 * ESZ + pr * 64;  // byte column of the pair in the wave's block
 #pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            const auto s0 = __builtin_amdgcn_permlane32_swap(pk[2 * p][0], pk[2 * p + 1][0], false, false);
-            const auto s1 = __builtin_amdgcn_permlane32_swap(pk[2 * p][1], pk[2 * p + 1][1], false, false);
-            (p == 0 ? lo[0] : hi[0]) = u32x4{s0[0], s1[0], s0[1], s1[1]};
-          }
-        } else {
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const float v0 = acc_read(acc[i][j][gq * 4 + 0]) * alpha, v1 = acc_read(acc[i][j][gq * 4 + 1]) * alpha;
-            const float v2 = acc_read(acc[i][j][gq * 4 + 2]) * alpha, v3 = acc_read(acc[i][j][gq * 4 + 3]) * alpha;
-            const u32x4 w = {__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2), __float_as_uint(v3)};
-            ((gq & 1) ? hi[gq >> 1] : lo[gq >> 1]) = w;
-          }
-        }
-        // row swap: lanes 0-15 give their hi piece to lanes 16-31 for their lo
-        // piece (and 32-47 / 48-63 alike), so that x holds rows 0-15 and y rows 16-31
-#pragma unroll
-        for (int pr = 0; pr < NPAIR; ++pr) {
-          u32x4 x, y;
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const auto sw = __builtin_amdgcn_permlane16_swap(lo[pr][d], hi[pr][d], false, false);
-            x[d] = sw[0];
-            y[d] = sw[1];
-          }
-          const int cb = j * 32 * ESZ + pr * 64;  // byte column of the pair in the wave's block
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            u32x4 v = half ? y : x;
-            gbyte* const cp = cw + (int64_t)(i * 32 + 16 * half) * ldc * ESZ + cb + loff;
-            if (interior) {
+            for (int half = 0; half < 2; ++half) {
+              u32x4 w = half ? ys[pr] : xs[pr];
+              gbyte* const cp = cw + (int64_t)(i * 32 + 16 * half) * ldc * ESZ + cb + loff;
               if constexpr (!OUT_BF16) {
                 if (g.accumulate) {
                   const u32x4 o = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(cp);
 #pragma unroll
-                  for (int d = 0; d < 4; ++d) v[d] = __float_as_uint(__uint_as_float(v[d]) + __uint_as_float(o[d]));
+                  for (int d = 0; d < 4; ++d) w[d] = __float_as_uint(__uint_as_float(w[d]) + __uint_as_float(o[d]));
                 }
               }
-              *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(cp) = v;
-            } else {
+              *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(cp) = w;
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TMW; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          u32x4 xs[NPAIR], ys[NPAIR];
+          tile_pieces<OUT_BF16>(acc[i][j], alpha, xs, ys);
+#pragma unroll
+          for (int pr = 0; pr < NPAIR; ++pr) {
+            const int cb = j * 32 * ESZ + pr * 64;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              u32x4 w = half ? ys[pr] : xs[pr];
+              gbyte* const cp = cw + (int64_t)(i * 32 + 16 * half) * ldc * ESZ + cb + loff;
               constexpr int PE = 16 / ESZ;  // elements per piece
               const int m = (int)bm0 + i * 32 + 16 * half + r16;
               const int n = (int)bn0 + cb / ESZ + pidx * PE;
@@ -507,20 +547,20 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
                       const u32x4 o = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(cp);
 #pragma unroll
                       for (int d = 0; d < 4; ++d)
-                        v[d] = __float_as_uint(__uint_as_float(v[d]) + __uint_as_float(o[d]));
+                        w[d] = __float_as_uint(__uint_as_float(w[d]) + __uint_as_float(o[d]));
                     }
                   }
-                  *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(cp) = v;
+                  *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(cp) = w;
                 } else {
 #pragma unroll
                   for (int e = 0; e < PE; ++e) {
                     if (n + e < g.N) {
                       if constexpr (OUT_BF16) {
                         reinterpret_cast<__attribute__((address_space(1))) uint16_t*>(cp)[e] =
-                            (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+                            (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
                       } else {
                         auto* ce = reinterpret_cast<__attribute__((address_space(1))) float*>(cp) + e;
-                        *ce = g.accumulate ? *ce + __uint_as_float(v[e]) : __uint_as_float(v[e]);
+                        *ce = g.accumulate ? *ce + __uint_as_float(w[e]) : __uint_as_float(w[e]);
                       }
                     }
                   }

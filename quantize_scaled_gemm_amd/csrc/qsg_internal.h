@@ -17,6 +17,13 @@ void launch_amax_update(float* history, int64_t L, int64_t step, const float* am
 void launch_cast_transpose(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                            int fmt, const float* scale, uint8_t* q, uint8_t* qt, float* amax_out,
                            hipStream_t st);
+// One delayed-scaling step of one tensor in a single launch: cast +
+// transpose with *scale, amax, history[step mod L] = amax and the next scale.
+// ws: two words, zero on entry, zero again on return.
+void launch_cast_transpose_delayed(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt,
+                                   int margin, float* history, int64_t L, int64_t step, float* scale,
+                                   float* scale_inv, uint8_t* q, uint8_t* qt, float* amax_out, uint32_t* ws,
+                                   hipStream_t st);
 void launch_quantize_blocked(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                              int scaling, int fmt, int margin, bool mx_ceil, uint8_t* q, void* s,
                              uint8_t* qt, void* st_, hipStream_t st);

@@ -54,15 +54,12 @@ __global__ void compute_scale_kernel(const float* amax, float fmax, int margin, 
   }
 }
 
-// One workgroup: history[step mod L] = amax; window max; next scale unless
-// the max is 0 or not finite ("Low-Precision Training Guide", recipe
-// "delayed", --fp8-amax-history-len / --fp8-amax-compute-algo max).
-__global__ __launch_bounds__(256) void amax_update_kernel(float* history, int64_t L, int64_t slot,
-                                                          const float* amax, float fmax,
-                                                          int margin, float* scale,
-                                                          float* scale_inv) {
-  __shared__ uint32_t red[4];
-  const uint32_t a = __float_as_uint(*amax);
+// One workgroup of 256 threads: history[slot] = amax (bits a); window max;
+// next scale unless the max is 0 or not finite ("Low-Precision Training
+// Guide", recipe "delayed", --fp8-amax-history-len / --fp8-amax-compute-algo
+// max).  red: 4 words of LDS.
+__device__ __forceinline__ void history_update_wg(float* history, int64_t L, int64_t slot, uint32_t a, float fmax,
+                                                  int margin, float* scale, float* scale_inv, uint32_t* red) {
   uint32_t m = 0;
   for (int64_t i = threadIdx.x; i < L; i += 256) {
     uint32_t v = (i == slot) ? a : __float_as_uint(history[i]);
@@ -84,6 +81,14 @@ __global__ __launch_bounds__(256) void amax_update_kernel(float* history, int64_
       *scale_inv = __fdiv_rn(1.0f, s);
     }
   }
+}
+
+__global__ __launch_bounds__(256) void amax_update_kernel(float* history, int64_t L, int64_t slot,
+                                                          const float* amax, float fmax,
+                                                          int margin, float* scale,
+                                                          float* scale_inv) {
+  __shared__ uint32_t red[4];
+  history_update_wg(history, L, slot, __float_as_uint(*amax), fmax, margin, scale, scale_inv, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -166,6 +171,14 @@ struct TileArgs {
   void* s;               // row-wise scales (MX: u8, block: f32)
   void* st;              // column-wise scales
   uint32_t* amax_out;    // MODE_TENSOR fused amax (as uint bits) or null
+  // MODE_TENSOR, one launch of a delayed-scaling step: ws[0] collects the
+  // amax bits, ws[1] counts finished workgroups; the last one records the
+  // amax in hist[slot], sets the next scale and clears ws again
+  uint32_t* ws;
+  float* hist;
+  int64_t hist_len, slot;
+  float* scale_w;        // the scale in force, replaced by the next one
+  float* scale_inv_w;
   int margin;
   bool mx_ceil;
   int64_t tiles_c, ntiles;
@@ -256,6 +269,61 @@ __device__ __forceinline__ void transpose4x4_bytes(uint32_t a, uint32_t b, uint3
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint32_t canon(uint32_t m) { return m > 0x7F800000u ? 0x7FC00000u : m; }
+
+// End of a one-launch delayed-scaling step (TileArgs::ws set).  Workgroups
+// are split into DELAYED_GROUPS groups (id mod DELAYED_GROUPS), each with its
+// own 128-byte line of the workspace holding the group's amax and arrival
+// count, so no address sees more than a few dozen atomics.  A workgroup
+// performs its group's atomic max and waits for it to return before it
+// arrives; the last arrival of a group arrives at the common counter; the
+// last one there has every workgroup's maximum in the group lines, records
+// the amax in the history, sets the next scale and clears the workspace.
+// Device-scope atomics are performed in issue order at the coherence point,
+// so no cache write-back is needed; the history, scale and FP8 outputs are
+// read by later launches only (the scale in force was read by every
+// workgroup before its first tile).
+constexpr int DELAYED_GROUPS = 32;
+constexpr int WS_LINE = 32;  // words per workspace line
+
+__device__ __forceinline__ void delayed_finish(const TileArgs& a, uint32_t m, float fmax, uint32_t* red) {
+  m = wave_max_u32(m);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < 4; ++i) m = m > red[i] ? m : red[i];
+    m = canon(m);
+    const uint32_t G = gridDim.x, grp = blockIdx.x % DELAYED_GROUPS;
+    const uint32_t ngrp = G < DELAYED_GROUPS ? G : DELAYED_GROUPS;
+    const uint32_t in_grp = G / DELAYED_GROUPS + (grp < G % DELAYED_GROUPS ? 1u : 0u);
+    uint32_t* line = a.ws + grp * WS_LINE;
+    uint32_t old = __hip_atomic_fetch_max(line, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" : "+v"(old) : : "memory");  // the max is performed before arriving
+    uint32_t last = 0;
+    if (__hip_atomic_fetch_add(line + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == in_grp - 1) {
+      const uint32_t n = __hip_atomic_fetch_add(a.ws + DELAYED_GROUPS * WS_LINE, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+      last = (n == ngrp - 1) ? 1u : 0u;
+    }
+    red[4] = last;
+    if (last) {
+      uint32_t am = 0;
+      for (uint32_t i = 0; i < ngrp; ++i) {
+        const uint32_t v = __hip_atomic_load(a.ws + i * WS_LINE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        am = am > v ? am : v;
+      }
+      for (uint32_t i = 0; i < ngrp; ++i) {
+        __hip_atomic_store(a.ws + i * WS_LINE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.ws + i * WS_LINE + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __hip_atomic_store(a.ws + DELAYED_GROUPS * WS_LINE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (a.amax_out) *a.amax_out = am;
+      red[5] = am;
+    }
+  }
+  __syncthreads();
+  if (red[4]) history_update_wg(a.hist, a.hist_len, a.slot, red[5], fmax, a.margin, a.scale_w, a.scale_inv_w, red + 8);
+}
 
 template <typename In, int MODE, int FMT>
 __global__ __launch_bounds__(256) void tile_kernel(TileArgs a) {
@@ -446,7 +514,11 @@ __global__ __launch_bounds__(256) void tile_kernel(TileArgs a) {
   }
 
   if constexpr (MODE == MODE_TENSOR) {
-    if (a.amax_out) block_max_to_global<256>(amax_acc, a.amax_out, &lds_red[0][0]);
+    if (a.ws) {
+      delayed_finish(a, amax_acc, FMAX, &lds_red[0][0]);
+    } else if (a.amax_out) {
+      block_max_to_global<256>(amax_acc, a.amax_out, &lds_red[0][0]);
+    }
   }
 }
 
@@ -552,6 +624,30 @@ void launch_cast_transpose(const void* x, int dtype, int64_t rows, int64_t cols,
   a.vec_ok = tile_vec_ok(x, dtype == 1 ? 2 : 4, rows, cols, ld, q, qt);
   a.scale = scale; a.q = q; a.qt = qt;
   a.amax_out = reinterpret_cast<uint32_t*>(amax_out);
+  a.tiles_c = (cols + TILE - 1) / TILE;
+  a.ntiles = ((rows + TILE - 1) / TILE) * a.tiles_c;
+  launch_tile_dtype<MODE_TENSOR>(a, dtype, fmt, st);
+}
+
+void launch_cast_transpose_delayed(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt,
+                                   int margin, float* history, int64_t L, int64_t step, float* scale,
+                                   float* scale_inv, uint8_t* q, uint8_t* qt, float* amax_out, uint32_t* ws,
+                                   hipStream_t st) {
+  if (rows == 0 || cols == 0) {
+    // nothing to quantize: the amax is 0 (ws[0] is 0 between calls)
+    if (amax_out) launch_fill_u32(reinterpret_cast<uint32_t*>(amax_out), 0u, 1, st);
+    launch_amax_update(history, L, step, reinterpret_cast<const float*>(ws), fmt, margin, scale, scale_inv, st);
+    return;
+  }
+  TileArgs a{};
+  a.x = x; a.rows = rows; a.cols = cols; a.ld = ld;
+  a.vec_ok = tile_vec_ok(x, dtype == 1 ? 2 : 4, rows, cols, ld, q, qt);
+  a.scale = scale; a.q = q; a.qt = qt;
+  a.amax_out = reinterpret_cast<uint32_t*>(amax_out);
+  a.ws = ws;
+  a.hist = history; a.hist_len = L; a.slot = step % L;
+  a.scale_w = scale; a.scale_inv_w = scale_inv;
+  a.margin = margin;
   a.tiles_c = (cols + TILE - 1) / TILE;
   a.ntiles = ((rows + TILE - 1) / TILE) * a.tiles_c;
   launch_tile_dtype<MODE_TENSOR>(a, dtype, fmt, st);

@@ -305,6 +305,83 @@ def test_delayed_trajectory(q, L, steps):
     assert np.array_equal(f32bits(to_np(hist)), f32bits(st.history))
 
 
+@pytest.mark.parametrize("L,steps,shape,fmt,dtype", [(4, 17, (256, 384), "e4m3", "bf16"),
+                                                     (16, 9, (200, 300), "e5m2", "bf16"),
+                                                     (1024, 6, (1024, 768), "e4m3", "f32")])
+def test_cast_transpose_delayed_one_launch(q, L, steps, shape, fmt, dtype):
+    """qsg_cast_transpose_delayed (cast + transpose, amax, history update in
+    one launch) follows the oracle's delayed trajectory bit for bit: bytes,
+    amax, scales and history, with an all-zero step and a step holding a NaN
+    (ragged 200 x 300 takes the element-wise edge tiles); the workspace is
+    zero again after every call."""
+    import torch
+
+    rows, cols = shape
+    code = q.FMT[fmt]
+    hist = torch.zeros(L, device="cuda")
+    scale = torch.ones(1, device="cuda")
+    scale_inv = torch.ones(1, device="cuda")
+    amax = torch.full((1,), 7.0, device="cuda")
+    ws = torch.zeros(q.DELAYED_WORKSPACE_BYTES // 4, dtype=torch.int32, device="cuda")
+    st = oracle.DelayedState(L, fmt, margin=1)
+    for t in range(steps):
+        xb = workloads.delayed_4096_step(t, rows, cols, out_cols=8)["X"]
+        if t % 7 == 3:
+            xb = np.zeros_like(xb)  # an all-zero step keeps the scale
+        xf = bf16_bits_to_f32(xb)
+        if t == 5 and L == 16:
+            xf = xf.copy()
+            xf[3, 7] = np.nan  # a NaN amax keeps the scale while it is in the window
+        xd = to_dev(xf) if dtype == "f32" else to_dev_bf16(workloads.f32_to_bf16_bits(xf) if t == 5 else xb)
+        qq, qt = empty_u8((rows, cols)), empty_u8((cols, rows))
+        q.qsg_cast_transpose_delayed(xd, code, 1, hist, t, scale, scale_inv, qq, qt, amax, ws)
+        rq, rqt, ra, used, _ = st.step(xf, t)
+        gq = to_np(qq)
+        nan = np.isnan(xf)
+        assert np.array_equal(gq[~nan], rq[~nan]), t
+        assert np.all((gq[nan] & 0x7F) == 0x7F)
+        assert np.array_equal(to_np(qt), gq.T), t
+        assert f32bits(to_np(amax))[0] == f32bits(ra)[()], t
+        assert f32bits(to_np(scale))[0] == f32bits(st.scale)[()], t
+        assert f32bits(to_np(scale_inv))[0] == f32bits(st.scale_inv)[()], t
+        assert not to_np(ws).any(), t
+    assert np.array_equal(f32bits(to_np(hist)), f32bits(st.history))
+
+
+def test_cast_transpose_delayed_matches_two_calls_and_empty(q):
+    """Against the two-call path (qsg_cast_transpose + qsg_amax_update) on the
+    delayed workload's shape, bit for bit; an empty tensor records amax 0."""
+    import torch
+
+    R, C, L = 1024, 4096, 1024
+    outs = {}
+    for path in ("one", "two"):
+        hist = torch.zeros(L, device="cuda")
+        scale, inv = torch.ones(1, device="cuda"), torch.ones(1, device="cuda")
+        amax = torch.zeros(1, device="cuda")
+        ws = torch.zeros(q.DELAYED_WORKSPACE_BYTES // 4, dtype=torch.int32, device="cuda")
+        qq, qt = empty_u8((R, C)), empty_u8((C, R))
+        for t in range(3):
+            xd = to_dev_bf16(workloads.delayed_4096_step(t, R, C, out_cols=8)["X"])
+            if path == "one":
+                q.qsg_cast_transpose_delayed(xd, q.E4M3, 0, hist, t, scale, inv, qq, qt, amax, ws)
+            else:
+                q.qsg_cast_transpose(xd, q.E4M3, scale, qq, qt, amax)
+                q.qsg_amax_update(hist, t, amax, q.E4M3, 0, scale, inv)
+        outs[path] = [to_np(x).copy() for x in (qq, qt, amax, scale, inv, hist)]
+    for a, b in zip(outs["one"], outs["two"]):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    hist = torch.full((4,), 3.0, device="cuda")
+    scale, inv = torch.ones(1, device="cuda"), torch.ones(1, device="cuda")
+    amax = torch.full((1,), 9.0, device="cuda")
+    ws = torch.zeros(q.DELAYED_WORKSPACE_BYTES // 4, dtype=torch.int32, device="cuda")
+    e = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    q.qsg_cast_transpose_delayed(e, q.E4M3, 0, hist, 6, scale, inv, None, None, amax, ws)
+    assert to_np(amax)[0] == 0.0
+    assert to_np(hist).tolist() == [3.0, 3.0, 0.0, 3.0]
+    assert to_np(scale)[0] == np.float32(448.0 / 3.0)
+
+
 def test_amax_update_nan_keeps_scale(q):
     import torch
 

@@ -196,6 +196,22 @@ int qsg_cast_transpose_delayed(const void* x, int dtype, int64_t rows, int64_t c
                                float* scale_dev, float* scale_inv_dev, uint8_t* q, uint8_t* qt,
                                float* amax_out_dev, void* workspace, void* stream);
 
+/* qsg_cast_transpose_delayed for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and results without `workspace`.  The
+ * library keeps the workspace in a file-scope device array of
+ * QSG_DELAYED_WORKSPACE_BYTES bytes, one copy per GPU, held until the process
+ * ends; its address is looked up on the first call on each device (that call
+ * also clears it), and every call leaves it zero.  The workspace need does not
+ * grow with the tensor, so no size is rejected for lack of scratch.  Calls on
+ * one GPU share the array: calls that overlap in time on one GPU (different
+ * streams without ordering) race and must not be issued.  Nothing is
+ * allocated or freed; a failed address lookup returns QSG_ERR_HIP. */
+int qsg_cast_transpose_delayed_noalloc(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt,
+                                       int margin, float* history_dev, int64_t hist_len, int64_t step,
+                                       float* scale_dev, float* scale_inv_dev, uint8_t* q, uint8_t* qt,
+                                       float* amax_out_dev, void* stream);
+
 /* FP8 store of the MLP activation's input, forward ("Benefits of Using FP8
  * Precision with MegaDLMs and Required Hardware", configuration field
  * activation_func_fp8_input_store: the activation's input is kept in FP8 for

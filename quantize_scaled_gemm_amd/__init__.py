@@ -32,6 +32,7 @@ ENTRY_POINTS = (
     "qsg_compute_scale",
     "qsg_cast_transpose",
     "qsg_cast_transpose_delayed",
+    "qsg_cast_transpose_delayed_noalloc",
     "qsg_amax_update",
     "qsg_quantize",
     "qsg_scaled_gemm",
@@ -77,6 +78,8 @@ def load_library(path=LIB_PATH):
     lib.qsg_cast_transpose.argtypes = [P, I, I64, I64, I64, I, F, P, P, F, P]
     lib.qsg_cast_transpose_delayed.restype = I
     lib.qsg_cast_transpose_delayed.argtypes = [P, I, I64, I64, I64, I, I, F, I64, I64, F, F, P, P, F, P, P]
+    lib.qsg_cast_transpose_delayed_noalloc.restype = I
+    lib.qsg_cast_transpose_delayed_noalloc.argtypes = [P, I, I64, I64, I64, I, I, F, I64, I64, F, F, P, P, F, P]
     lib.qsg_amax_update.restype = I
     lib.qsg_amax_update.argtypes = [F, I64, I64, F, I, I, I, F, F, P]
     lib.qsg_quantize.restype = I
@@ -244,6 +247,23 @@ def qsg_cast_transpose_delayed(x, fmt, margin, history, step, scale, scale_inv, 
                                                      _ptr(history), history.numel(), step, _ptr(scale),
                                                      _ptr(scale_inv), _ptr(q), _ptr(qt), _ptr(amax_out),
                                                      _ptr(workspace), _stream(stream)))
+
+
+def qsg_cast_transpose_delayed_noalloc(x, fmt, margin, history, step, scale, scale_inv, q=None, qt=None,
+                                       amax_out=None, stream=None):
+    """qsg_cast_transpose_delayed with the library's own per-GPU workspace
+    (no allocation; overlapping calls on one GPU race)."""
+    rows, cols, ld = _matrix(x)
+    _buffer(history, "history", history.numel(), "f32")
+    for t, n in ((scale, "scale"), (scale_inv, "scale_inv")):
+        _buffer(t, n, 1, "f32")
+    _buffer(q, "q", rows * cols, "u8", required=False)
+    _buffer(qt, "qt", rows * cols, "u8", required=False)
+    _buffer(amax_out, "amax_out", 1, "f32", required=False)
+    _check(load_library().qsg_cast_transpose_delayed_noalloc(_ptr(x), _dtype_code(x), rows, cols, ld, fmt, margin,
+                                                             _ptr(history), history.numel(), step, _ptr(scale),
+                                                             _ptr(scale_inv), _ptr(q), _ptr(qt), _ptr(amax_out),
+                                                             _stream(stream)))
 
 
 def qsg_amax_update(history, step, amax, fmt, margin, scale, scale_inv, algo=AMAX_MAX, stream=None):

@@ -119,6 +119,29 @@ int qsg_cast_transpose_delayed(const void* x, int dtype, int64_t rows, int64_t c
   return check_launch(fn);
 }
 
+int qsg_cast_transpose_delayed_noalloc(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt,
+                                       int margin, float* history_dev, int64_t hist_len, int64_t step,
+                                       float* scale_dev, float* scale_inv_dev, uint8_t* q, uint8_t* qt,
+                                       float* amax_out_dev, void* stream) {
+  const char* fn = "qsg_cast_transpose_delayed_noalloc";
+  int rc = check_matrix(fn, x, dtype, rows, cols, ld);
+  if (rc) return rc;
+  if (!valid_fmt(fmt)) return fail(QSG_ERR_ARG, "%s: bad fmt %d", fn, fmt);
+  if (margin < 0 || margin > 64) return fail(QSG_ERR_ARG, "%s: margin %d outside [0, 64]", fn, margin);
+  if (!history_dev || !scale_dev || !scale_inv_dev) return fail(QSG_ERR_ARG, "%s: null pointer", fn);
+  if (hist_len < 1) return fail(QSG_ERR_ARG, "%s: hist_len %lld < 1", fn, (long long)hist_len);
+  if (step < 0) return fail(QSG_ERR_ARG, "%s: negative step", fn);
+  const bool empty = rows == 0 || cols == 0;
+  if (!q && !qt && !empty) return fail(QSG_ERR_ARG, "%s: q and qt are both null", fn);
+  if (amax_out_dev && !aligned(amax_out_dev, 4)) return fail(QSG_ERR_ALIGN, "%s: amax_out not aligned", fn);
+  uint32_t* ws = nullptr;
+  if (qsg::delayed_scratch(&ws, as_stream(stream)) != 0)
+    return fail(QSG_ERR_HIP, "%s: the device address of the library's scratch array could not be found", fn);
+  qsg::launch_cast_transpose_delayed(x, dtype, rows, cols, ld, fmt, margin, history_dev, hist_len, step, scale_dev,
+                                     scale_inv_dev, q, qt, amax_out_dev, ws, as_stream(stream));
+  return check_launch(fn);
+}
+
 int qsg_act_fp8_store_fwd(const void* h, int64_t rows, int64_t cols, int64_t ld, int fmt, const float* scale_dev,
                           void* a, uint8_t* q, float* amax_out_dev, void* stream) {
   const char* fn = "qsg_act_fp8_store_fwd";

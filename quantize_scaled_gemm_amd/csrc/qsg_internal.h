@@ -24,6 +24,10 @@ void launch_cast_transpose_delayed(const void* x, int dtype, int64_t rows, int64
                                    int margin, float* history, int64_t L, int64_t step, float* scale,
                                    float* scale_inv, uint8_t* q, uint8_t* qt, float* amax_out, uint32_t* ws,
                                    hipStream_t st);
+// Device address of this GPU's file-scope workspace for the allocation-free
+// delayed step (looked up once per device; the first lookup also clears it on
+// `st`).  Returns 0, or a negative code when the lookup fails.
+int delayed_scratch(uint32_t** out, hipStream_t st);
 void launch_quantize_blocked(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                              int scaling, int fmt, int margin, bool mx_ceil, uint8_t* q, void* s,
                              uint8_t* qt, void* st_, hipStream_t st);

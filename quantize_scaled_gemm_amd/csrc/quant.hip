@@ -27,6 +27,9 @@
 // the fused amax of the per-tensor path costs one atomic per workgroup.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
+#include "qsg.h"
 #include "qsg_device.h"
 #include "qsg_internal.h"
 
@@ -651,6 +654,32 @@ void launch_cast_transpose_delayed(const void* x, int dtype, int64_t rows, int64
   a.tiles_c = (cols + TILE - 1) / TILE;
   a.ntiles = ((rows + TILE - 1) / TILE) * a.tiles_c;
   launch_tile_dtype<MODE_TENSOR>(a, dtype, fmt, st);
+}
+
+// ---------------------------------------------------------------------------
+// allocation-free variant of the one-launch delayed step: the workspace is a
+// file-scope device array, one copy per GPU, whose address is looked up once
+// per device (the host-side name of the array is not a device address)
+// ---------------------------------------------------------------------------
+constexpr int kScratchWords = (DELAYED_GROUPS + 1) * WS_LINE;  // 4224 bytes
+static_assert(kScratchWords * 4 == QSG_DELAYED_WORKSPACE_BYTES, "workspace size of include/qsg.h");
+static __device__ __attribute__((aligned(256))) uint32_t scratch[kScratchWords];
+
+int delayed_scratch(uint32_t** out, hipStream_t st) {
+  static std::mutex mu;
+  static uint32_t* ptr[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return -2;
+    ptr[dev] = reinterpret_cast<uint32_t*>(p);
+    // zero at load; cleared once more on first use, then every call leaves it zero
+    launch_fill_u32(ptr[dev], 0u, kScratchWords, st);
+  }
+  *out = ptr[dev];
+  return 0;
 }
 
 void launch_quantize_blocked(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,

@@ -165,6 +165,12 @@ __shared__ __attribute__((aligned(256))) uint32_t lds_sa0[FBM];
 __shared__ __attribute__((aligned(256))) uint32_t lds_sa1[FBM];
 __shared__ __attribute__((aligned(256))) uint32_t lds_sb0[FBN];
 __shared__ __attribute__((aligned(256))) uint32_t lds_sb1[FBN];
+// MXFP8 with grouped scale fetches: 16 bytes (4 K tiles) per row, two groups
+// in flight; row r's word for K tile k of the group is word 4r + k
+__shared__ __attribute__((aligned(1024))) uint32_t lds_gsa0[FBM * 4];
+__shared__ __attribute__((aligned(1024))) uint32_t lds_gsa1[FBM * 4];
+__shared__ __attribute__((aligned(1024))) uint32_t lds_gsb0[FBN * 4];
+__shared__ __attribute__((aligned(1024))) uint32_t lds_gsb1[FBN * 4];
 
 template <int S>
 __device__ __forceinline__ uint8_t* stage_a() { return S ? lds_a1 : lds_a0; }
@@ -174,16 +180,26 @@ template <int S>
 __device__ __forceinline__ uint32_t* stage_sa() { return S ? lds_sa1 : lds_sa0; }
 template <int S>
 __device__ __forceinline__ uint32_t* stage_sb() { return S ? lds_sb1 : lds_sb0; }
+template <int GB>
+__device__ __forceinline__ uint32_t* group_sa() { return GB ? lds_gsa1 : lds_gsa0; }
+template <int GB>
+__device__ __forceinline__ uint32_t* group_sb() { return GB ? lds_gsb1 : lds_gsb0; }
+
+// Scale handling of a kernel instance: SC_NONE per-tensor (one scale pair in
+// the epilogue); SC_MX E8M0 bytes fetched with every K tile (4 bytes per row);
+// SC_MXG E8M0 bytes fetched once per group of 4 K tiles (16 bytes per row,
+// a quarter of the fetch instructions, each covering 64 rows).
+constexpr int SC_NONE = 0, SC_MX = 1, SC_MXG = 2;
 
 // Fetch of K tile kt of a tile into stage S: part 0 = the A tile (+ MX
 // scale words), part 1 = the B tile; `wl` is this wave's 1 KB block offset.
-template <int S, int PART, bool MX, int TN>
+template <int S, int PART, int SC, int TN>
 __device__ __forceinline__ void issue_part(const TileRes& t, const uint32_t (&voa)[NCHUNK],
                                            const uint32_t (&vob)[NCHUNK], uint32_t vos, uint32_t wl, uint32_t kt) {
   if constexpr (PART == 0) {
 #pragma unroll
     for (int i = 0; i < NCHUNK; ++i) dma16(t.ra, voa[i], kt * FBK, stage_a<S>() + i * 4096 + wl);
-    if constexpr (MX) {
+    if constexpr (SC == SC_MX) {
       dma4(t.rsa, vos, kt * 4, stage_sa<S>() + wl / 16);
       dma4(t.rsb, vos, kt * 4, stage_sb<S>() + wl / 16);
     }
@@ -193,11 +209,20 @@ __device__ __forceinline__ void issue_part(const TileRes& t, const uint32_t (&vo
   }
 }
 
-template <int S, bool MX, int TN>
+template <int S, int SC, int TN>
 __device__ __forceinline__ void issue_stage(const TileRes& t, const uint32_t (&voa)[NCHUNK],
                                             const uint32_t (&vob)[NCHUNK], uint32_t vos, uint32_t wl, uint32_t kt) {
-  issue_part<S, 0, MX, TN>(t, voa, vob, vos, wl, kt);
-  issue_part<S, 1, MX, TN>(t, voa, vob, vos, wl, kt);
+  issue_part<S, 0, SC, TN>(t, voa, vob, vos, wl, kt);
+  issue_part<S, 1, SC, TN>(t, voa, vob, vos, wl, kt);
+}
+
+// SC_MXG: the E8M0 bytes of scale group grp (K tiles 4 grp .. 4 grp + 3) of
+// the tile's 256 A rows and 256 B rows into group buffer GB: lane L of wave w
+// fetches the 16 bytes of row 64 w + L.
+template <int GB>
+__device__ __forceinline__ void issue_scale_group(const TileRes& t, uint32_t vos, uint32_t wl, uint32_t grp) {
+  dma16(t.rsa, vos, grp * 16, reinterpret_cast<uint8_t*>(group_sa<GB>()) + wl);
+  dma16(t.rsb, vos, grp * 16, reinterpret_cast<uint8_t*>(group_sb<GB>()) + wl);
 }
 // s_waitcnt vmcnt(N) lgkmcnt(0)
 template <int N>
@@ -215,14 +240,22 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 
-template <int S, bool MX, int TN>
+// Fragments of one 64-K step from stage S, and for MXFP8 the scale words of
+// the step's rows: from the stage's per-K-tile buffers (SC_MX) or word KI of
+// each row in group buffer GB (SC_MXG).
+template <int S, int SC, int GB, int KI, int TN>
 __device__ __forceinline__ void load_frags(Frags<TN>& f, int kk, int a_row_off, int b_row_off, int c_lo, int c_hi,
                                            int a_srow, int b_srow, int sh) {
 #pragma unroll
   for (int i = 0; i < TMW; ++i) f.a[i] = ffrag(stage_a<S>(), a_row_off, i, c_lo, c_hi);
 #pragma unroll
   for (int j = 0; j < TN; ++j) f.b[j] = ffrag(stage_b<S>(), b_row_off, j, c_lo, c_hi);
-  if constexpr (MX) {
+  if constexpr (SC == SC_MXG) {
+#pragma unroll
+    for (int i = 0; i < TMW; ++i) f.sa[i] = (int)(group_sa<GB>()[(a_srow + i * 32) * 4 + KI] >> sh);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) f.sb[j] = (int)(group_sb<GB>()[(b_srow + j * 32) * 4 + KI] >> sh);
+  } else if constexpr (SC == SC_MX) {
 #pragma unroll
     for (int i = 0; i < TMW; ++i) f.sa[i] = (int)(stage_sa<S>()[a_srow + i * 32] >> sh);
 #pragma unroll
@@ -328,8 +361,9 @@ __device__ __forceinline__ void tile_coords(const FastArgs& g, uint32_t logical,
   n0 = ((logical % per_group) / gsize) * (TN * 64);
 }
 
-template <bool MX, int FA, int FB, bool OUT_BF16, int TN>
+template <int SC, int FA, int FB, bool OUT_BF16, int TN>
 __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
+  constexpr bool MX = SC != SC_NONE;
   constexpr int WM = FBM / 2, WN = TN * 32, TBN = TN * 64;
   constexpr int NQ = TMW * TN;  // MFMAs per 64-K step
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -346,7 +380,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
   const uint32_t x_wgs = G / 8 + (xcd < G % 8 ? 1 : 0);
   uint32_t logical = x_begin + local;
   if (logical >= x_end) return;
-  const uint32_t nk = (uint32_t)(g.K / FBK);  // even (checked by the launcher)
+  const uint32_t nk = (uint32_t)(g.K / FBK);  // even; SC_MXG: a multiple of 8 (checked by the launcher)
   const uint32_t nb = (uint32_t)(g.K / 32);   // MX: E8M0 bytes per row
 
   // fragment addressing: lane half h reads chunks kk*4 + h and kk*4 + 2 + h
@@ -381,16 +415,17 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
   tile_coords<TN>(g, logical, m0, n0);
   TileRes cur = resources(m0, n0);
   constexpr int P1 = TN == 4 ? 8 : 5, P2 = TN == 4 ? 8 : 3;
-  constexpr int NA = NCHUNK + (MX ? 2 : 0);                 // fetches in a part-0 issue
-  constexpr int NS = NCHUNK * (4 + TN) / 4 + (MX ? 2 : 0);  // fetches of a whole stage
-  issue_stage<0, MX, TN>(cur, voa, vob, vos, wl, 0);
-  issue_stage<1, MX, TN>(cur, voa, vob, vos, wl, 1);
+  constexpr int NA = NCHUNK + (SC == SC_MX ? 2 : 0);                 // fetches in a part-0 issue
+  constexpr int NS = NCHUNK * (4 + TN) / 4 + (SC == SC_MX ? 2 : 0);  // fetches of a whole stage
+  if constexpr (SC == SC_MXG) issue_scale_group<0>(cur, vos, wl, 0);  // lands with stage 0
+  issue_stage<0, SC, TN>(cur, voa, vob, vos, wl, 0);
+  issue_stage<1, SC, TN>(cur, voa, vob, vos, wl, 1);
   wait_vm_lgkm0<NS>();  // stage 0 landed
   lds_barrier();
 
   v16f acc[TMW][TN];
   Frags<TN> f0, f1;
-  load_frags<0, MX, TN>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);
+  load_frags<0, SC, 0, 0, TN>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);
   while (true) {
     // The next tile's resources: the fetches of the last two K steps go to
     // its first two K tiles (or repeat this tile's, past the last tile), so
@@ -418,13 +453,15 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
   //      fragments are read from S^1 and the B half of the K tile two ahead
   //      is fetched into S.
   // Two ahead of the last K tiles are the next tile's first two.
-#define QSG_FAST_STEP(S, KT)                                                                   \
+#define QSG_FAST_STEP(S, KT, GB, KI)                                                           \
   {                                                                                            \
     const bool own = (KT) + 2 < nk;                                                            \
     TileRes RES = own ? cur : nxt_t;                                                           \
     uint32_t FK = own ? (KT) + 2 : (KT) + 2 - nk;                                              \
-    pin_res<MX>(RES, FK);                                                                          \
-    load_frags<S, MX, TN>(f1, 1, a_row_off, b_row_off, c10, c11, a_srow, b_srow, sh1);         \
+    pin_res<MX>(RES, FK);                                                                      \
+    constexpr bool SGF = SC == SC_MXG && (KI) == 1;  /* this step fetches the next scale group */ \
+    constexpr int NAS = NA + (SGF ? 2 : 0);                                                    \
+    load_frags<S, SC, GB, KI, TN>(f1, 1, a_row_off, b_row_off, c10, c11, a_srow, b_srow, sh1); \
     mfma_range<MX, FA, FB, 0, P1>(acc, f0);                                                    \
     _Pragma("unroll") for (int q = 0; q < P1 - 1; ++q) {                                       \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
@@ -434,20 +471,30 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     __builtin_amdgcn_sched_barrier(0);                                                         \
     wait_vm_lgkm0<63>();                                                                       \
     lds_barrier();                                                                             \
-    issue_part<S, 0, MX, TN>(RES, voa, vob, vos, wl, FK);                                      \
+    issue_part<S, 0, SC, TN>(RES, voa, vob, vos, wl, FK);                                      \
+    if constexpr (SGF) {                                                                       \
+      /* the next group of this tile, or the next tile's first group */                        \
+      const uint32_t ng = (KT) / 4 + 1;                                                        \
+      const bool sown = ng < nk / 4;                                                           \
+      TileRes SRES = sown ? cur : nxt_t;                                                       \
+      uint32_t SG = sown ? ng : 0;                                                             \
+      pin_res<MX>(SRES, SG);                                                                   \
+      issue_scale_group<(GB) ^ 1>(SRES, vos, wl, SG);                                          \
+    }                                                                                          \
     mfma_range<MX, FA, FB, P1, NQ>(acc, f0);                                                   \
     mfma_range<MX, FA, FB, 0, P2>(acc, f1);                                                    \
-    _Pragma("unroll") for (int q = 0; q < (NA < NQ - P1 + P2 ? NA : NQ - P1 + P2); ++q) {      \
+    _Pragma("unroll") for (int q = 0; q < (NAS < NQ - P1 + P2 ? NAS : NQ - P1 + P2); ++q) {    \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);                                       \
       __builtin_amdgcn_sched_group_barrier(0x001, 3, 1);                                       \
     }                                                                                          \
-    if constexpr (NQ - P1 + P2 > NA)                                                           \
-      __builtin_amdgcn_sched_group_barrier(0x008, NQ - P1 + P2 - NA, 1);                       \
+    if constexpr (NQ - P1 + P2 > NAS)                                                          \
+      __builtin_amdgcn_sched_group_barrier(0x008, NQ - P1 + P2 - NAS, 1);                      \
     __builtin_amdgcn_sched_barrier(0);                                                         \
-    wait_vm_lgkm0<NA>();                                                                       \
+    wait_vm_lgkm0<NAS>();                                                                      \
     lds_barrier();                                                                             \
-    load_frags<S ^ 1, MX, TN>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);     \
-    issue_part<S, 1, MX, TN>(RES, voa, vob, vos, wl, FK);                                      \
+    load_frags<S ^ 1, SC, ((KI) == 3 ? (GB) ^ 1 : (GB)), (((KI) + 1) & 3), TN>(                \
+        f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);                           \
+    issue_part<S, 1, SC, TN>(RES, voa, vob, vos, wl, FK);                                      \
     mfma_range<MX, FA, FB, P2, NQ>(acc, f1);                                                   \
     _Pragma("unroll") for (int q = 0; q < NQ - P2 - 1; ++q) {                                  \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);                                       \
@@ -460,13 +507,29 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
 
     // nk >= 2: a do-while leaves the compiler no path that skips the loop
     // (merging the zeroed accumulators of such a path with the loop's costs
-    // accumulator copies and spills in the epilogue)
+    // accumulator copies and spills in the epilogue).  With grouped scale
+    // fetches one iteration covers two scale groups (8 K tiles), so the group
+    // buffer of every step is a compile-time choice.
     uint32_t kt = 0;
-    do {
-      QSG_FAST_STEP(0, kt)
-      QSG_FAST_STEP(1, kt + 1)
-      kt += 2;
-    } while (kt < nk);
+    if constexpr (SC == SC_MXG) {
+      do {
+        QSG_FAST_STEP(0, kt, 0, 0)
+        QSG_FAST_STEP(1, kt + 1, 0, 1)
+        QSG_FAST_STEP(0, kt + 2, 0, 2)
+        QSG_FAST_STEP(1, kt + 3, 0, 3)
+        QSG_FAST_STEP(0, kt + 4, 1, 0)
+        QSG_FAST_STEP(1, kt + 5, 1, 1)
+        QSG_FAST_STEP(0, kt + 6, 1, 2)
+        QSG_FAST_STEP(1, kt + 7, 1, 3)
+        kt += 8;
+      } while (kt < nk);
+    } else {
+      do {
+        QSG_FAST_STEP(0, kt, 0, 0)
+        QSG_FAST_STEP(1, kt + 1, 0, 0)
+        kt += 2;
+      } while (kt < nk);
+    }
 #undef QSG_FAST_STEP
     // The next tile's first K tile is in stage 0, its second on the way to
     // stage 1.  The epilogue stores from registers and waits for no fetch.
@@ -579,7 +642,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     m0 = nm0;
     n0 = nn0;
     cur = nxt_t;
-    load_frags<0, MX, TN>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);
+    load_frags<0, SC, 0, 0, TN>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);
   }
 }
 
@@ -595,29 +658,29 @@ int device_cu_count() {
   return cached[dev];
 }
 
-template <bool MX, int FA, int FB>
+template <int SC, int FA, int FB>
 void launch_fast_cfg(const FastArgs& g, bool out_bf16, int tn, hipStream_t st) {
   const int64_t tiles = g.tiles_m * g.tiles_n;
   const unsigned grid = (unsigned)(tiles < g.max_wgs ? tiles : g.max_wgs);
   if (tn == 4) {
     if (out_bf16)
-      hipLaunchKernelGGL((gemm_fast_kernel<MX, FA, FB, true, 4>), dim3(grid), dim3(256), 0, st, g);
+      hipLaunchKernelGGL((gemm_fast_kernel<SC, FA, FB, true, 4>), dim3(grid), dim3(256), 0, st, g);
     else
-      hipLaunchKernelGGL((gemm_fast_kernel<MX, FA, FB, false, 4>), dim3(grid), dim3(256), 0, st, g);
+      hipLaunchKernelGGL((gemm_fast_kernel<SC, FA, FB, false, 4>), dim3(grid), dim3(256), 0, st, g);
   } else {
     if (out_bf16)
-      hipLaunchKernelGGL((gemm_fast_kernel<MX, FA, FB, true, 2>), dim3(grid), dim3(256), 0, st, g);
+      hipLaunchKernelGGL((gemm_fast_kernel<SC, FA, FB, true, 2>), dim3(grid), dim3(256), 0, st, g);
     else
-      hipLaunchKernelGGL((gemm_fast_kernel<MX, FA, FB, false, 2>), dim3(grid), dim3(256), 0, st, g);
+      hipLaunchKernelGGL((gemm_fast_kernel<SC, FA, FB, false, 2>), dim3(grid), dim3(256), 0, st, g);
   }
 }
 
-template <bool MX>
+template <int SC>
 void launch_fast_fmt(const FastArgs& g, int fa, int fb, bool out_bf16, int tn, hipStream_t st) {
-  if (fa == kE4M3 && fb == kE4M3) launch_fast_cfg<MX, kE4M3, kE4M3>(g, out_bf16, tn, st);
-  else if (fa == kE5M2 && fb == kE4M3) launch_fast_cfg<MX, kE5M2, kE4M3>(g, out_bf16, tn, st);
-  else if (fa == kE4M3 && fb == kE5M2) launch_fast_cfg<MX, kE4M3, kE5M2>(g, out_bf16, tn, st);
-  else launch_fast_cfg<MX, kE5M2, kE5M2>(g, out_bf16, tn, st);
+  if (fa == kE4M3 && fb == kE4M3) launch_fast_cfg<SC, kE4M3, kE4M3>(g, out_bf16, tn, st);
+  else if (fa == kE5M2 && fb == kE4M3) launch_fast_cfg<SC, kE5M2, kE4M3>(g, out_bf16, tn, st);
+  else if (fa == kE4M3 && fb == kE5M2) launch_fast_cfg<SC, kE4M3, kE5M2>(g, out_bf16, tn, st);
+  else launch_fast_cfg<SC, kE5M2, kE5M2>(g, out_bf16, tn, st);
 }
 
 }  // namespace
@@ -643,11 +706,16 @@ bool launch_scaled_gemm_fast(const uint8_t* a, int fa, bool mx, const void* sa, 
   g.tiles_m = tiles_m;
   g.tiles_n = tiles_n;
   g.max_wgs = device_cu_count();
+  // MXFP8 scale bytes in groups of 4 K tiles when whole pairs of groups fit
+  // every tile's K (16-byte aligned rows of scale bytes)
+  const bool mx_grouped = mx && K % (8 * FBK) == 0;
   auto launch = [&](const FastArgs& ga, int tn) {
-    if (mx)
-      launch_fast_fmt<true>(ga, fa, fb, out_bf16, tn, st);
+    if (mx_grouped)
+      launch_fast_fmt<SC_MXG>(ga, fa, fb, out_bf16, tn, st);
+    else if (mx)
+      launch_fast_fmt<SC_MX>(ga, fa, fb, out_bf16, tn, st);
     else
-      launch_fast_fmt<false>(ga, fa, fb, out_bf16, tn, st);
+      launch_fast_fmt<SC_NONE>(ga, fa, fb, out_bf16, tn, st);
   };
   // A last round that would leave at least half of the workgroups idle, made
   // of whole tile-rows: those rows run as a second launch of 256 x 128 tiles

@@ -384,10 +384,12 @@ def test_large_tile_partial_last_round(q, out):
     assert np.array_equal(y, want)
 
 
-def test_large_tile_mx_partial_last_round(q):
+@pytest.mark.parametrize("K", [512, 3072])
+def test_large_tile_mx_partial_last_round(q, K):
     """MXFP8 on the same tile grid: the E8M0 rows of the last tile-rows come
-    from the offset scale block of the second launch."""
-    M, N, K = 14336 - 20, 4096, 512
+    from the offset scale block of the second launch.  K = 3072 takes the
+    grouped scale fetch (16 bytes per row per 4 K tiles, 6 groups)."""
+    M, N = 14336 - 20, 4096
     g = workloads.generator(55)
     ia = g.integers(-8, 9, (M, K))
     ib = g.integers(-8, 9, (N, K))
@@ -400,11 +402,14 @@ def test_large_tile_mx_partial_last_round(q):
     assert np.array_equal(y, f32_to_bf16_rne_f64(ref))
 
 
-def test_large_tile_mx_persistent_edge_tiles(q):
+@pytest.mark.parametrize("K", [512, 2048])
+def test_large_tile_mx_persistent_edge_tiles(q, K):
     """MXFP8 through the persistent path with ragged M and N and several
     tiles per workgroup: power-of-two block scales on integer codes keep every
-    product and partial sum exact, so the result is exact."""
-    M, N, K = 4096 + 72, 8192 + 24, 512
+    product and partial sum exact, so the result is exact.  K = 2048 takes
+    the grouped scale fetch, whose next-tile prefetch crosses tile
+    boundaries."""
+    M, N = 4096 + 72, 8192 + 24
     g = workloads.generator(53)
     ia = g.integers(-8, 9, (M, K))
     ib = g.integers(-8, 9, (N, K))

@@ -352,7 +352,11 @@ void launch_scaled_gemm(const uint8_t* a, int fa, int ka, const void* sa, const 
   if ((per_tensor || ka == 2) &&
       launch_scaled_gemm_fast(a, fa, ka == 2, sa, b, fb, sb, M, N, K, lda, ldb, c, c_dtype, ldc, accumulate, st))
     return;
-  // (the 128 x 128 blockwise kernel only writes C; accumulation uses the general kernel)
+  // (the blockwise large-tile kernels only write C; accumulation uses the general kernel)
+  if (ka == 3 && (kb == 4 || kb == 3) && !accumulate &&
+      launch_scaled_gemm_block2(a, fa, reinterpret_cast<const float*>(sa), b, fb, reinterpret_cast<const float*>(sb),
+                                kb == 4, M, N, K, lda, ldb, c, c_dtype, ldc, st))
+    return;
   if (ka == 3 && kb == 4 && !accumulate &&
       launch_scaled_gemm_block_fast(a, fa, reinterpret_cast<const float*>(sa), b, fb,
                                     reinterpret_cast<const float*>(sb), true, M, N, K, lda, ldb, c, c_dtype, ldc,

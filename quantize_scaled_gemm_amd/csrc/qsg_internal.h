@@ -44,6 +44,13 @@ bool launch_scaled_gemm_fast(const uint8_t* a, int fa, bool mx, const void* sa, 
 bool launch_scaled_gemm_block_fast(const uint8_t* a, int fa, const float* sa, const uint8_t* b, int fb,
                                    const float* sb, bool w128, int64_t M, int64_t N, int64_t K, int64_t lda,
                                    int64_t ldb, void* c, int c_dtype, int64_t ldc, hipStream_t st);
+// 256x256 eight-wave kernel for blockwise scales (16x16x128 instructions, one
+// per 128-K block and 16 x 16 tile): w128 = 128 x 128 weight blocks on B
+// (fprop, dgrad), else 1 x 128 blocks on both operands (wgrad); returns false
+// (and launches nothing) when the problem is not eligible.
+bool launch_scaled_gemm_block2(const uint8_t* a, int fa, const float* sa, const uint8_t* b, int fb, const float* sb,
+                               bool w128, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, void* c,
+                               int c_dtype, int64_t ldc, hipStream_t st);
 // GeLU of h with the FP8 store of h (forward) and the GeLU gradient from the
 // stored FP8 input (backward); bf16 h / da with leading dimension ld, dense
 // a / dh / q.

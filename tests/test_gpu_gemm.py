@@ -346,6 +346,58 @@ def test_block_fast_wide_scales(q):
     assert np.isfinite(y).all()
 
 
+# ---------------------------------------------------------------------------
+# the eight-wave blockwise path (256 x 256 tiles, one 16x16x128 instruction per
+# 128-K block and 16 x 16 tile; used when K % 1024 == 0, E4M3 weights and at
+# least 128 such tiles)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("w128", [True, False])
+@pytest.mark.parametrize("M,N,K,out", [(4096 + 100, 2048 + 40, 1024, "f32"), (8192 + 16, 4096 + 8, 3072, "bf16")])
+def test_block2_integer_exact(q, w128, M, N, K, out):
+    """Integer-valued codes and power-of-two block scales keep every partial
+    and running sum exact in binary32, so the result must equal the exact one
+    (bf16: its correctly rounded value) whatever the summation order: this
+    pins the fragment, scale-row and output layouts, ragged M and N, and
+    (second shape: 561 tiles) the persistent tile walk and the next tile's
+    prefetch across tile boundaries."""
+    g = workloads.generator(58, M, N, K, int(w128))
+    ia = g.integers(-4, 5, (M, K))
+    ib = g.integers(-4, 5, (N, K))
+    qa = oracle.encode(ia.astype(np.float32), "e4m3")
+    qb = oracle.encode(ib.astype(np.float32), "e4m3")
+    sa = np.exp2(g.integers(-1, 2, (M, K // 128))).astype(np.float32)
+    if w128:
+        sb = np.exp2(g.integers(-1, 2, ((N + 127) // 128, K // 128))).astype(np.float32)
+    else:
+        sb = np.exp2(g.integers(-1, 2, (N, K // 128))).astype(np.float32)
+    ref = oracle.gemm_block(qa, "e4m3", sa, qb, "e4m3", sb, "128x128" if w128 else "1x128")
+    y = gemm(q, to_dev(qa), 0, 3, to_dev(sa), to_dev(qb), 0, 4 if w128 else 3, to_dev(sb), out=out)
+    if out == "f32":
+        assert np.array_equal(y, ref)
+    else:
+        assert np.array_equal(y, f32_to_bf16_rne_f64(ref))
+
+
+@pytest.mark.parametrize("w128,fa", [(True, 0), (True, 1), (False, 0)])
+def test_block2_random_codes_wide_scales(q, w128, fa):
+    """Random codes over the whole E4M3 / E5M2 range, block scales over 12
+    binades, ragged N: the eight-wave path against the fp64 oracle on a
+    256-row band (R10)."""
+    M, N, K = 4096, 4096 + 100, 2048
+    g = workloads.generator(59, int(w128), fa)
+    qa = rand_codes(g, (M, K), FMT_NAMES[fa])
+    qb = rand_codes(g, (N, K), "e4m3")
+    sa = np.exp2(g.uniform(-20, -8, (M, K // 128))).astype(np.float32)
+    rows_b = (N + 127) // 128 if w128 else N
+    sb = np.exp2(g.uniform(-20, -8, (rows_b, K // 128))).astype(np.float32)
+    y = gemm(q, to_dev(qa), fa, 3, to_dev(sa), to_dev(qb), 0, 4 if w128 else 3, to_dev(sb), out="f32")
+    rows = slice(1024, 1280)
+    ref = oracle.gemm_block(qa[rows], FMT_NAMES[fa], sa[rows], qb, "e4m3", sb, "128x128" if w128 else "1x128")
+    ok, info = oracle.tolerance_check(y[rows], ref)
+    assert ok, info
+    assert np.isfinite(y).all()
+
+
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_large_tile_persistent_edge_tiles(q, out):
     """More tiles than CUs with a ragged last tile-row and tile-column: each

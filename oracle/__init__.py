@@ -62,6 +62,7 @@ from .gemm import (  # noqa: F401
     mx_operand,
     mfma_accumulation_bound,
 )
+from . import nvfp4  # noqa: F401  (NVFP4: E2M1 elements, E4M3 1x16 block scales, fp32 tensor scale)
 from .activation import (  # noqa: F401
     gelu,
     gelu_grad,

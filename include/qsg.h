@@ -331,6 +331,56 @@ int qsg_scaled_gemm_accumulate(const uint8_t* a, int fa, int ka, const void* sa,
                                int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
                                float* c, int64_t ldc, void* stream);
 
+/* NVFP4 block scaling ("Low-Precision Training Guide": recipe "nvfp4",
+ * "NVFP4 block scaling", --fp4-format e2m1; table "Hardware and Recipe
+ * Compatibility", row nvfp4).  The pages name the element format only; the
+ * block size and the scale formats follow NVIDIA's NVFP4 definition, outside
+ * the pages: 16 consecutive elements along a row share one E4M3 decode scale
+ * byte, and the tensor has one fp32 scale
+ *     s_enc = fp32(448 * 6 / amax)   (1 for amax 0 or not finite, FLT_MAX
+ *                                      when the quotient overflows),
+ *     s_dec = fp32(1 / s_enc).
+ * A block with maximum |x| = b is quantized with one binary32 operation per
+ * step, each rounded to nearest even:
+ *     S    = dec(E4M3(fp32(fp32(b / 6) * s_enc)))   (saturating RNE E4M3)
+ *     m    = fp32(s_enc / S), or 0 when S is 0 or the scale byte is NaN
+ *     code = E2M1(fp32(x * m))
+ * E2M1 (OCP FP4): magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 with a sign bit;
+ * saturating round to nearest, a midpoint going to the even code; the sign
+ * of zero is kept; NaN gives sign | 6.  The value represented is
+ * dec(code) * S * s_dec.
+ *
+ * tensor_scale_dev  out: 3 floats {amax, s_enc, s_dec} (device).
+ * q   rows x (cols/2) bytes, two codes per byte along the row, element 2i in
+ *     the low nibble;  s  rows x (cols/16) E4M3 bytes;       cols % 16 == 0.
+ * qt  cols x (rows/2) bytes: the column-wise copy (blocks of 16 rows, stored
+ *     transposed, same packing);  st  cols x (rows/16);      rows % 16 == 0.
+ * Pass NULL for (q, s) or (qt, st) to skip a copy.  q and qt must be 4-byte
+ * aligned.  An empty matrix writes {0, 1, 1} to tensor_scale_dev only. */
+int qsg_quantize_nvfp4(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                       float* tensor_scale_dev, uint8_t* q, uint8_t* s, uint8_t* qt, uint8_t* st,
+                       void* stream);
+
+/* GEMM on NVFP4 operands (same pages and definition as qsg_quantize_nvfp4):
+ *
+ *     C[m, n] = (s_dec_a * s_dec_b) * sum_k (dec(A[m, k]) * Sa(m, k / 16))
+ *                                         * (dec(B[n, k]) * Sb(n, k / 16))
+ *
+ * A is M x K codes packed as qsg_quantize_nvfp4 writes them (lda bytes per
+ * row, lda >= K/2), B is N x K (ldb); sa (M x K/16) and sb (N x K/16) are
+ * their dense E4M3 block-scale bytes; sdec_a_dev / sdec_b_dev point at the
+ * s_dec float of each operand (element 2 of its tensor_scale).  K % 16 == 0.
+ * Each block-scaled value is exact in bfloat16; products are exact and are
+ * summed in fp32.  C is M x N (ldc) in c_dtype (QSG_BF16 rounded to nearest
+ * even, or QSG_F32), aligned to its element size; fprop, dgrad and wgrad take
+ * this form with the row-wise or column-wise copies as for qsg_scaled_gemm.
+ * The vector path needs A and B 16-byte aligned with lda, ldb multiples of
+ * 16 (else bytes are read one by one).  K == 0 writes zeros. */
+int qsg_gemm_nvfp4(const uint8_t* a, const uint8_t* sa, const float* sdec_a_dev,
+                   const uint8_t* b, const uint8_t* sb, const float* sdec_b_dev,
+                   int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                   void* c, int c_dtype, int64_t ldc, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

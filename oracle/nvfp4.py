@@ -186,6 +186,14 @@ def _quantize_rows(x, s_enc):
     return encode_e2m1(v), code
 
 
+def quantize_rows(x, s_enc):
+    """Row-wise NVFP4 of some rows of a tensor whose tensor scale s_enc is
+    already known (each row's blocks depend only on the row and s_enc):
+    (packed q, E4M3 scale bytes)."""
+    c, s = _quantize_rows(np.ascontiguousarray(x, dtype=np.float32), np.float32(s_enc))
+    return pack(c), s
+
+
 def quantize(x, rowwise=True, colwise=True):
     """NVFP4 row-wise (blocks of 16 along a row) and column-wise (blocks of 16
     along a column, stored transposed) copies of a float32 matrix.  Returns a

@@ -40,6 +40,8 @@ ENTRY_POINTS = (
     "qsg_act_fp8_store_fwd",
     "qsg_act_fp8_store_bwd",
     "qsg_wgrad_bf16",
+    "qsg_quantize_nvfp4",
+    "qsg_gemm_nvfp4",
 )
 
 
@@ -94,6 +96,8 @@ def load_library(path=LIB_PATH):
     lib.qsg_act_fp8_store_bwd.restype = I
     lib.qsg_act_fp8_store_bwd.argtypes = [P, I64, I64, I64, I, P, F, P, P]
     lib.qsg_scaled_gemm_accumulate.argtypes = [P, I, I, P, P, I, I, P, I64, I64, I64, I64, I64, P, I64, P]
+    lib.qsg_quantize_nvfp4.argtypes = [P, I, I64, I64, I64, P, P, P, P, P, P]
+    lib.qsg_gemm_nvfp4.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, P, I, I64, P]
     _lib = lib
     return lib
 
@@ -386,3 +390,44 @@ def qsg_wgrad_bf16(dy, x, c, accumulate=False, stream=None):
         raise QsgError(f"C is {Nc}x{Kc}, expected {N}x{K}")
     _check(load_library().qsg_wgrad_bf16(_ptr(dy), T, N, lddy, _ptr(x), K, ldx, _ptr(c), _dtype_code(c), ldc,
                                          1 if accumulate else 0, _stream(stream)))
+
+
+def qsg_quantize_nvfp4(x, tensor_scale, q=None, s=None, qt=None, st=None, stream=None):
+    """NVFP4 copies of x: tensor_scale (3 fp32: amax, s_enc, s_dec); row-wise
+    q (rows x cols/2 packed E2M1) with s (rows x cols/16 E4M3 bytes) and/or
+    column-wise qt (cols x rows/2) with st (cols x rows/16)."""
+    rows, cols, ld = _matrix(x)
+    _buffer(tensor_scale, "tensor_scale", 3, "f32")
+    if q is not None and cols % 16 == 0:
+        _buffer(q, "q", rows * (cols // 2), "u8")
+        _buffer(s, "s", rows * (cols // 16), "u8")
+    if qt is not None and rows % 16 == 0:
+        _buffer(qt, "qt", cols * (rows // 2), "u8")
+        _buffer(st, "st", cols * (rows // 16), "u8")
+    _check(load_library().qsg_quantize_nvfp4(_ptr(x), _dtype_code(x), rows, cols, ld, _ptr(tensor_scale),
+                                             _ptr(q), _ptr(s), _ptr(qt), _ptr(st), _stream(stream)))
+
+
+def qsg_gemm_nvfp4(a, sa, ts_a, b, sb, ts_b, c, stream=None):
+    """C (M x N) = s_dec_a s_dec_b (A Sa)(B Sb)^T on NVFP4 operands: a is
+    M x K/2 packed bytes, b is N x K/2, sa / sb their E4M3 block scales
+    (M x K/16, N x K/16), ts_a / ts_b their 3-float tensor scales (element 2,
+    s_dec, is what the library reads)."""
+    M, Kh, lda = _matrix(a)
+    N, Khb, ldb = _matrix(b)
+    if Khb != Kh:
+        raise QsgError(f"K mismatch: A has {2 * Kh}, B has {2 * Khb}")
+    K = 2 * Kh
+    Mc, Nc, ldc = _matrix(c)
+    if (Mc, Nc) != (M, N):
+        raise QsgError(f"C is {Mc}x{Nc}, expected {M}x{N}")
+    _gemm_operands(a, b)
+    if K % 16 == 0:
+        _buffer(sa, "sa", M * (K // 16), "u8")
+        _buffer(sb, "sb", N * (K // 16), "u8")
+    _buffer(ts_a, "ts_a", 3, "f32")
+    _buffer(ts_b, "ts_b", 3, "f32")
+    sdec_a = _ptr(ts_a) + 8 if not isinstance(ts_a, int) else ts_a
+    sdec_b = _ptr(ts_b) + 8 if not isinstance(ts_b, int) else ts_b
+    _check(load_library().qsg_gemm_nvfp4(_ptr(a), _ptr(sa), sdec_a, _ptr(b), _ptr(sb), sdec_b, M, N, K, lda, ldb,
+                                         _ptr(c), _dtype_code(c), ldc, _stream(stream)))

@@ -301,4 +301,47 @@ int qsg_scaled_gemm_accumulate(const uint8_t* a, int fa, int ka, const void* sa,
                      ldc, true, stream);
 }
 
+int qsg_quantize_nvfp4(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, float* tensor_scale_dev,
+                       uint8_t* q, uint8_t* s, uint8_t* qt, uint8_t* st, void* stream) {
+  const char* fn = "qsg_quantize_nvfp4";
+  int rc = check_matrix(fn, x, dtype, rows, cols, ld);
+  if (rc) return rc;
+  if (!tensor_scale_dev) return fail(QSG_ERR_ARG, "%s: null tensor_scale", fn);
+  if (!aligned(tensor_scale_dev, 4)) return fail(QSG_ERR_ALIGN, "%s: tensor_scale not 4-byte aligned", fn);
+  const bool empty = rows == 0 || cols == 0;
+  const bool row = q != nullptr, col = qt != nullptr;
+  if (!row && !col && !empty) return fail(QSG_ERR_ARG, "%s: q and qt are both null", fn);
+  if ((row && !s) || (col && !st)) return fail(QSG_ERR_ARG, "%s: a requested copy has a null scale tensor", fn);
+  if ((q && !aligned(q, 4)) || (qt && !aligned(qt, 4))) return fail(QSG_ERR_ALIGN, "%s: q / qt not 4-byte aligned", fn);
+  if (row && cols % 16)
+    return fail(QSG_ERR_SHAPE, "%s: row-wise blocks need cols %% 16 == 0 (cols %lld)", fn, (long long)cols);
+  if (col && rows % 16)
+    return fail(QSG_ERR_SHAPE, "%s: column-wise blocks need rows %% 16 == 0 (rows %lld)", fn, (long long)rows);
+  qsg::launch_quantize_nvfp4(x, dtype, rows, cols, ld, q, s, qt, st, tensor_scale_dev, as_stream(stream));
+  return check_launch(fn);
+}
+
+int qsg_gemm_nvfp4(const uint8_t* a, const uint8_t* sa, const float* sdec_a_dev, const uint8_t* b, const uint8_t* sb,
+                   const float* sdec_b_dev, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, void* c,
+                   int c_dtype, int64_t ldc, void* stream) {
+  const char* fn = "qsg_gemm_nvfp4";
+  if (!valid_dtype(c_dtype)) return fail(QSG_ERR_ARG, "%s: bad output dtype", fn);
+  if (M < 0 || N < 0 || K < 0) return fail(QSG_ERR_ARG, "%s: negative shape", fn);
+  if (K % 16) return fail(QSG_ERR_SHAPE, "%s: NVFP4 needs K %% 16 == 0 (K %lld)", fn, (long long)K);
+  if (M == 0 || N == 0) return QSG_OK;
+  if ((M + 127) / 128 > 65535 || (N + 127) / 128 > 0x7FFFFFFF)
+    return fail(QSG_ERR_UNSUPPORTED, "%s: M %lld exceeds 65535 tiles of 128 rows", fn, (long long)M);
+  if (!c) return fail(QSG_ERR_ARG, "%s: null C", fn);
+  if (ldc < N) return fail(QSG_ERR_ARG, "%s: ldc < N", fn);
+  if (!aligned(c, c_dtype == QSG_BF16 ? 2 : 4)) return fail(QSG_ERR_ALIGN, "%s: C not aligned to its element size", fn);
+  if (!sdec_a_dev || !sdec_b_dev) return fail(QSG_ERR_ARG, "%s: null tensor scale", fn);
+  if (!aligned(sdec_a_dev, 4) || !aligned(sdec_b_dev, 4)) return fail(QSG_ERR_ALIGN, "%s: tensor scales not aligned", fn);
+  if (K > 0) {
+    if (!a || !b || !sa || !sb) return fail(QSG_ERR_ARG, "%s: null operand or block scales", fn);
+    if (lda < K / 2 || ldb < K / 2) return fail(QSG_ERR_ARG, "%s: lda/ldb < K/2 bytes", fn);
+  }
+  qsg::launch_gemm_nvfp4(a, sa, sdec_a_dev, b, sb, sdec_b_dev, M, N, K, lda, ldb, c, c_dtype, ldc, as_stream(stream));
+  return check_launch(fn);
+}
+
 }  // extern "C"

@@ -62,6 +62,15 @@ void launch_act_fp8_store_bwd(const void* da, int64_t rows, int64_t cols, int64_
 // row-major bf16); accumulate for fp32 C only.
 void launch_wgrad_bf16(const void* dy, int64_t T, int64_t N, int64_t lddy, const void* x, int64_t K, int64_t ldx,
                        void* c, int c_dtype, int64_t ldc, bool accumulate, hipStream_t st);
+// NVFP4: ts = {amax, s_enc, s_dec} written on `st`; row-wise (q, s) and/or
+// column-wise (qt, st_) copies with E4M3 scales per 16 elements.
+void launch_quantize_nvfp4(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, uint8_t* q, uint8_t* s,
+                           uint8_t* qt, uint8_t* st_, float* ts, hipStream_t st);
+// C = (s_dec_a s_dec_b) * sum of block-scaled E2M1 products; A M x K and B
+// N x K packed (lda, ldb in bytes), sa / sb dense E4M3 bytes (K / 16 per row).
+void launch_gemm_nvfp4(const uint8_t* a, const uint8_t* sa, const float* ta, const uint8_t* b, const uint8_t* sb,
+                       const float* tb, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, void* c,
+                       int c_dtype, int64_t ldc, hipStream_t st);
 void launch_scaled_gemm(const uint8_t* a, int fa, int ka, const void* sa, const uint8_t* b, int fb,
                         int kb, const void* sb, int64_t M, int64_t N, int64_t K, int64_t lda,
                         int64_t ldb, void* c, int c_dtype, int64_t ldc, bool accumulate, hipStream_t st);

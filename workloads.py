@@ -25,6 +25,8 @@ Workloads (shapes and distributions of the FP8 Linear configurations):
                    ~N(0,1e-3)
   blockwise_7168   X 16384x7168, W 18432x7168 Student-t (nu=3); dY
                    16384x18432 Student-t (nu=3) x 1e-3 for the backward GEMMs
+  nvfp4_4096       X 16384x4096, W 14336x4096 ~N(0,0.02); dY 16384x14336
+                   ~N(0,1e-3) (the mxfp8_4096 shapes, NVFP4 operands)
   linear_4096      X 32768x4096 ~N(0,1); W 4096x4096 and W2 14336x4096
                    ~N(0,0.02); dY 32768x4096 and dY2 32768x14336 ~N(0,1e-3)
 """
@@ -43,6 +45,7 @@ WORKLOAD_IDS = {
     "mxfp8_4096": 3,
     "blockwise_7168": 4,
     "linear_4096": 5,
+    "nvfp4_4096": 6,
 }
 
 
@@ -155,3 +158,11 @@ def linear_4096(m=32768, h=4096, f=14336, which=("X", "W", "W2", "dY", "dY2")):
         "dY2": ([w, 4], (m, f), 1e-3),
     }
     return {k: normal(spec[k][0], spec[k][1], spec[k][2]) for k in which}
+
+
+def nvfp4_4096(m=16384, n=14336, k=4096, with_dy=False):
+    w = WORKLOAD_IDS["nvfp4_4096"]
+    out = {"X": normal([w, 0], (m, k), 0.02), "W": normal([w, 1], (n, k), 0.02)}
+    if with_dy:
+        out["dY"] = normal([w, 2], (m, n), 1e-3)
+    return out

@@ -68,6 +68,8 @@ struct FastArgs {
   bool accumulate;  // fp32 C only: C = fp32(C + result)
   int64_t tiles_m, tiles_n;
   int64_t max_wgs;  // persistent grid: one workgroup per CU
+  const float* ta;  // NVFP4: the operands' per-tensor decode scales
+  const float* tb;
 };
 
 // 16-byte chunk c of LDS row r is stored at position c ^ row_swizzle(r).  A
@@ -361,10 +363,115 @@ __device__ __forceinline__ void tile_coords(const FastArgs& g, uint32_t logical,
   n0 = ((logical % per_group) / gsize) * (TN * 64);
 }
 
+// Epilogue of one workgroup tile: scale by alpha, convert, store straight
+// from registers (see tile_pieces); every store writes 16 rows x 64
+// contiguous bytes.  (cm0, cn0): the tile's first row and column.
+template <bool OUT_BF16, int TN>
+__device__ __forceinline__ void store_tile(const FastArgs& g, v16f (&acc)[TMW][TN], float alpha, int64_t cm0,
+                                           int64_t cn0, int wm, int wn, int lane) {
+  constexpr int WM = FBM / 2, WN = TN * 32, TBN = TN * 64;
+  constexpr int ESZ = OUT_BF16 ? 2 : 4;
+  // tile coordinates made opaque here, so that no address below is
+  // computed ahead of the K loop and kept live across it
+  uint32_t em0 = (uint32_t)cm0, en0 = (uint32_t)cn0;
+  int64_t ldc = g.ldc;
+  gbyte* cbase = (gbyte*)g.c;
+  asm volatile("" : "+s"(em0), "+s"(en0), "+s"(ldc), "+s"(cbase));
+  const int64_t bm0 = (int64_t)em0 + wm * WM, bn0 = (int64_t)en0 + wn * WN;
+  int elane = lane;
+  asm volatile("" : "+v"(elane));
+  const int eh = elane >> 5;
+  const bool interior = g.vec_c && bm0 - wm * WM + FBM <= g.M && bn0 - wn * WN + TBN <= g.N;
+  gbyte* const cw = cbase + (bm0 * ldc + bn0) * ESZ;  // wave-uniform
+  // After the swaps below, a store writes 16 rows x 64 contiguous bytes:
+  // lane l holds row (l % 16) (+16 for the second store of a pair) and the
+  // 16-byte piece pidx = l / 32 + 2 ((l / 16) % 2) of the pair's 64 bytes.
+  const int r16 = elane & 15, pidx = eh + 2 * ((elane >> 4) & 1);
+  const uint32_t loff = ((uint32_t)r16 * (uint32_t)ldc * ESZ) + (uint32_t)pidx * 16;
+  constexpr int NPAIR = OUT_BF16 ? 1 : 2;  // 64-byte column pairs per 32 x 32 tile
+  if (interior) {
+    // every piece of the workgroup's tile is inside C: straight-line code
+    // with no per-tile branch, one scheduling region per accumulator tile
+#pragma unroll
+    for (int i = 0; i < TMW; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        u32x4 xs[NPAIR], ys[NPAIR];
+        tile_pieces<OUT_BF16>(acc[i][j], alpha, xs, ys);
+#pragma unroll
+        for (int pr = 0; pr < NPAIR; ++pr) {
+          const int cb = j * 32 * ESZ + pr * 64;  // byte column of the pair in the wave's block
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            u32x4 w = half ? ys[pr] : xs[pr];
+            gbyte* const cp = cw + (int64_t)(i * 32 + 16 * half) * ldc * ESZ + cb + loff;
+            if constexpr (!OUT_BF16) {
+              if (g.accumulate) {
+                const u32x4 o = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(cp);
+#pragma unroll
+                for (int d = 0; d < 4; ++d) w[d] = __float_as_uint(__uint_as_float(w[d]) + __uint_as_float(o[d]));
+              }
+            }
+            *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(cp) = w;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TMW; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        u32x4 xs[NPAIR], ys[NPAIR];
+        tile_pieces<OUT_BF16>(acc[i][j], alpha, xs, ys);
+#pragma unroll
+        for (int pr = 0; pr < NPAIR; ++pr) {
+          const int cb = j * 32 * ESZ + pr * 64;
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            u32x4 w = half ? ys[pr] : xs[pr];
+            gbyte* const cp = cw + (int64_t)(i * 32 + 16 * half) * ldc * ESZ + cb + loff;
+            constexpr int PE = 16 / ESZ;  // elements per piece
+            const int m = (int)bm0 + i * 32 + 16 * half + r16;
+            const int n = (int)bn0 + cb / ESZ + pidx * PE;
+            if (m < g.M) {
+              if (g.vec_c && n + PE <= g.N) {
+                if constexpr (!OUT_BF16) {
+                  if (g.accumulate) {
+                    const u32x4 o = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(cp);
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                      w[d] = __float_as_uint(__uint_as_float(w[d]) + __uint_as_float(o[d]));
+                  }
+                }
+                *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(cp) = w;
+              } else {
+#pragma unroll
+                for (int e = 0; e < PE; ++e) {
+                  if (n + e < g.N) {
+                    if constexpr (OUT_BF16) {
+                      reinterpret_cast<__attribute__((address_space(1))) uint16_t*>(cp)[e] =
+                          (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                    } else {
+                      auto* ce = reinterpret_cast<__attribute__((address_space(1))) float*>(cp) + e;
+                      *ce = g.accumulate ? *ce + __uint_as_float(w[e]) : __uint_as_float(w[e]);
+                    }
+                  }
+                }
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
 template <int SC, int FA, int FB, bool OUT_BF16, int TN>
 __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
   constexpr bool MX = SC != SC_NONE;
-  constexpr int WM = FBM / 2, WN = TN * 32, TBN = TN * 64;
+  constexpr int WM = FBM / 2, WN = TN * 32;
   constexpr int NQ = TMW * TN;  // MFMAs per 64-K step
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -536,104 +643,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     // (The last step's reads of f0 are repeated after it, so that the
     // fragments are not held through the epilogue.)
 
-    // ---- epilogue: scale, convert, store straight from registers (see
-    // tile_pieces); every store writes 16 rows x 64 contiguous bytes ----
-    constexpr int ESZ = OUT_BF16 ? 2 : 4;
-    // tile coordinates made opaque here, so that no address below is
-    // computed ahead of the K loop and kept live across it
-    uint32_t em0 = (uint32_t)cm0, en0 = (uint32_t)cn0;
-    int64_t ldc = g.ldc;
-    gbyte* cbase = (gbyte*)g.c;
-    asm volatile("" : "+s"(em0), "+s"(en0), "+s"(ldc), "+s"(cbase));
-    const int64_t bm0 = (int64_t)em0 + wm * WM, bn0 = (int64_t)en0 + wn * WN;
-    int elane = lane;
-    asm volatile("" : "+v"(elane));
-    const int eh = elane >> 5;
-    const bool interior = g.vec_c && bm0 - wm * WM + FBM <= g.M && bn0 - wn * WN + TBN <= g.N;
-    gbyte* const cw = cbase + (bm0 * ldc + bn0) * ESZ;  // wave-uniform
-    // After the swaps below, a store writes 16 rows x 64 contiguous bytes:
-    // lane l holds row (l % 16) (+16 for the second store of a pair) and the
-    // 16-byte piece pidx = l / 32 + 2 ((l / 16) % 2) of the pair's 64 bytes.
-    const int r16 = elane & 15, pidx = eh + 2 * ((elane >> 4) & 1);
-    const uint32_t loff = ((uint32_t)r16 * (uint32_t)ldc * ESZ) + (uint32_t)pidx * 16;
-    constexpr int NPAIR = OUT_BF16 ? 1 : 2;  // 64-byte column pairs per 32 x 32 tile
-    if (interior) {
-      // every piece of the workgroup's tile is inside C: straight-line code
-      // with no per-tile branch, one scheduling region per accumulator tile
-#pragma unroll
-      for (int i = 0; i < TMW; ++i) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          u32x4 xs[NPAIR], ys[NPAIR];
-          tile_pieces<OUT_BF16>(acc[i][j], alpha, xs, ys);
-#pragma unroll
-          for (int pr = 0; pr < NPAIR; ++pr) {
-            const int cb = j * 32 * ESZ + pr * 64;  // byte column of the pair in the wave's block
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-              u32x4 w = half ? ys[pr] : xs[pr];
-              gbyte* const cp = cw + (int64_t)(i * 32 + 16 * half) * ldc * ESZ + cb + loff;
-              if constexpr (!OUT_BF16) {
-                if (g.accumulate) {
-                  const u32x4 o = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(cp);
-#pragma unroll
-                  for (int d = 0; d < 4; ++d) w[d] = __float_as_uint(__uint_as_float(w[d]) + __uint_as_float(o[d]));
-                }
-              }
-              *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(cp) = w;
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < TMW; ++i) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          u32x4 xs[NPAIR], ys[NPAIR];
-          tile_pieces<OUT_BF16>(acc[i][j], alpha, xs, ys);
-#pragma unroll
-          for (int pr = 0; pr < NPAIR; ++pr) {
-            const int cb = j * 32 * ESZ + pr * 64;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-              u32x4 w = half ? ys[pr] : xs[pr];
-              gbyte* const cp = cw + (int64_t)(i * 32 + 16 * half) * ldc * ESZ + cb + loff;
-              constexpr int PE = 16 / ESZ;  // elements per piece
-              const int m = (int)bm0 + i * 32 + 16 * half + r16;
-              const int n = (int)bn0 + cb / ESZ + pidx * PE;
-              if (m < g.M) {
-                if (g.vec_c && n + PE <= g.N) {
-                  if constexpr (!OUT_BF16) {
-                    if (g.accumulate) {
-                      const u32x4 o = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(cp);
-#pragma unroll
-                      for (int d = 0; d < 4; ++d)
-                        w[d] = __float_as_uint(__uint_as_float(w[d]) + __uint_as_float(o[d]));
-                    }
-                  }
-                  *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(cp) = w;
-                } else {
-#pragma unroll
-                  for (int e = 0; e < PE; ++e) {
-                    if (n + e < g.N) {
-                      if constexpr (OUT_BF16) {
-                        reinterpret_cast<__attribute__((address_space(1))) uint16_t*>(cp)[e] =
-                            (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-                      } else {
-                        auto* ce = reinterpret_cast<__attribute__((address_space(1))) float*>(cp) + e;
-                        *ce = g.accumulate ? *ce + __uint_as_float(w[e]) : __uint_as_float(w[e]);
-                      }
-                    }
-                  }
-                }
-              }
-            }
-          }
-        }
-      }
-    }
+    store_tile<OUT_BF16, TN>(g, acc, alpha, cm0, cn0, wm, wn, lane);
     if (!more) {
       wait_vm_lgkm0<0>();  // the repeated fetches of the last step land before the workgroup ends
       break;
@@ -643,6 +653,245 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     n0 = nn0;
     cur = nxt_t;
     load_frags<0, SC, 0, 0, TN>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 operands ("Low-Precision Training Guide": recipe "nvfp4", E2M1
+// elements; NVIDIA's NVFP4 definition: one E4M3 decode scale per 16 elements
+// along K and an fp32 decode scale per tensor):
+//   C[m,n] = ta tb sum_k (dec(A[m,k]) Sa(m,k/16)) (dec(B[n,k]) Sb(n,k/16)).
+// A block-scaled value dec(code) * S has at most 6 significant bits and lies
+// in [2^-10, 2688], so it is exact in f16; the products are exact in the
+// f32 accumulation of v_mfma_f32_32x32x16_f16.  (gfx950's FP4 matrix
+// instructions take power-of-two scales per 32 elements, which cannot carry
+// an E4M3 scale per 16, and its scaled FP4 conversions use only the scale's
+// exponent: the conversion runs with scale 1 and the block scale is applied
+// by v_pk_mul_f16.)
+//   * The same 256 x 256 workgroup tile, waves and LDS stages as the FP8
+//     kernel: a K tile is 256 elements = 128 bytes of codes per row, fetched
+//     global -> LDS with the FP8 chunk mapping and swizzle; the tile's 16
+//     scale bytes per row travel to the group buffers (16 B per row).
+//   * Each wave decodes its own fragments from LDS.  For a 64-K chunk of a
+//     K tile, lane half h reads the 16 bytes (32 codes) of K [32h, 32h + 32)
+//     of its row with one ds_read_b128; step s = 0..3 of the chunk feeds
+//     codes 8s .. 8s + 7 of them to the 16-K MFMA.  A and B lanes of the same
+//     half see the same K, so the chunk's 64 K values are each multiplied
+//     once; the steps' K order differs from the plain one, which only
+//     changes the order of the f32 sums.  The two blocks a lane half covers
+//     per chunk are scale bytes 2h (steps 0, 1) and 2h + 1 (steps 2, 3) of
+//     the row's chunk word.
+//   * Decoding step t + 1 (4 conversions + 4 packed multiplies per 8 values)
+//     is interleaved with the 16 MFMAs of step t.  One barrier per K tile:
+//     at step 12 every wave has read the tile's last chunk, the next K tile
+//     has landed, the stage is refilled with the K tile two ahead, and the
+//     next K tile's first chunk is read.
+// ---------------------------------------------------------------------------
+typedef _Float16 nv_h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 nv_h8 __attribute__((ext_vector_type(8)));
+
+constexpr int NV_KT = 256;          // elements per K tile (FBK bytes of codes per row)
+constexpr int NV_FETCHES = 2 * NCHUNK + 2;  // global -> LDS loads per thread per K tile
+
+// 8 codes (element 2i in the low nibble of byte i) times the scale pair s2.
+__device__ __forceinline__ nv_h8 nv_decode8(uint32_t w, nv_h2 s2) {
+  const nv_h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  const nv_h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  const nv_h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  const nv_h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  return nv_h8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// The raw data of one 64-K chunk for this lane: 16 bytes of codes per
+// fragment row, and the row's scale word shifted so that byte 0 / 1 are the
+// blocks of steps 0-1 / 2-3.
+struct NvChunk {
+  u32x4 a[TMW], b[4];
+  uint32_t sa[TMW], sb[4];
+};
+
+template <int S>
+__device__ __forceinline__ void nv_read_chunk(NvChunk& r, int c, int slot, int a_row_off, int b_row_off, int a_srow,
+                                              int b_srow, int sh) {
+#pragma unroll
+  for (int i = 0; i < TMW; ++i)
+    r.a[i] = *reinterpret_cast<const u32x4*>(stage_a<S>() + a_row_off + i * 32 * FBK + slot);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    r.b[j] = *reinterpret_cast<const u32x4*>(stage_b<S>() + b_row_off + j * 32 * FBK + slot);
+#pragma unroll
+  for (int i = 0; i < TMW; ++i) r.sa[i] = group_sa<S>()[(a_srow + i * 32) * 4 + c] >> sh;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r.sb[j] = group_sb<S>()[(b_srow + j * 32) * 4 + c] >> sh;
+}
+
+// Fragments of step s (0..3) of a chunk.
+__device__ __forceinline__ void nv_frags(const NvChunk& r, int s, nv_h8 (&fa)[TMW], nv_h8 (&fb)[4]) {
+#pragma unroll
+  for (int i = 0; i < TMW; ++i) {
+    const nv_h2 sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sa[i], 1.0f, false);
+    const nv_h2 s2 = s < 2 ? __builtin_shufflevector(sp, sp, 0, 0) : __builtin_shufflevector(sp, sp, 1, 1);
+    fa[i] = nv_decode8(r.a[i][s], s2);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const nv_h2 sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sb[j], 1.0f, false);
+    const nv_h2 s2 = s < 2 ? __builtin_shufflevector(sp, sp, 0, 0) : __builtin_shufflevector(sp, sp, 1, 1);
+    fb[j] = nv_decode8(r.b[j][s], s2);
+  }
+}
+
+// K tile kt of a tile into stage S: codes of A and B, then the 16 scale bytes
+// of each row (lane L of wave w: row 64 w + L).
+template <int S>
+__device__ __forceinline__ void nv_issue(const TileRes& t, const uint32_t (&voa)[NCHUNK], const uint32_t (&vob)[NCHUNK],
+                                         uint32_t vos, uint32_t wl, uint32_t kt) {
+#pragma unroll
+  for (int i = 0; i < NCHUNK; ++i) dma16(t.ra, voa[i], kt * FBK, stage_a<S>() + i * 4096 + wl);
+#pragma unroll
+  for (int i = 0; i < NCHUNK; ++i) dma16(t.rb, vob[i], kt * FBK, stage_b<S>() + i * 4096 + wl);
+  dma16(t.rsa, vos, kt * 16, reinterpret_cast<uint8_t*>(group_sa<S>()) + wl);
+  dma16(t.rsb, vos, kt * 16, reinterpret_cast<uint8_t*>(group_sb<S>()) + wl);
+}
+
+// Per-lane addressing of the NVFP4 kernel.
+struct NvAddr {
+  int slot[4];  // swizzled byte offset of chunk c's 16 bytes for this lane half
+  int a_row_off, b_row_off, a_srow, b_srow, sh;
+};
+
+// One K tile in stage S.  On entry r0 holds its first chunk and (fa, fb) the
+// fragments of its first step; on return r0 holds the next K tile's first
+// chunk (stage S ^ 1) and (fa, fb) that K tile's first-step fragments.  At
+// step 12 the stage is refilled with K tile fk of `res`.
+template <int S>
+__device__ __forceinline__ void nv_ktile(v16f (&acc)[TMW][4], NvChunk& r0, nv_h8 (&fa)[TMW], nv_h8 (&fb)[4],
+                                         const NvAddr& ad, TileRes res, uint32_t fk, const uint32_t (&voa)[NCHUNK],
+                                         const uint32_t (&vob)[NCHUNK], uint32_t vos, uint32_t wl) {
+  NvChunk rc = r0, rn;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int c = t / 4, s = t % 4;
+    if (s == 1 && c < 3) nv_read_chunk<S>(rn, c + 1, ad.slot[c + 1], ad.a_row_off, ad.b_row_off, ad.a_srow, ad.b_srow, ad.sh);
+    if (t == 12) {
+      pin_res<true>(res, fk);
+      wait_vm_lgkm0<0>();
+      lds_barrier();
+      nv_issue<S>(res, voa, vob, vos, wl, fk);
+      nv_read_chunk<S ^ 1>(r0, 0, ad.slot[0], ad.a_row_off, ad.b_row_off, ad.a_srow, ad.b_srow, ad.sh);
+    }
+    nv_h8 na[TMW], nb[4];
+    if (t < 15)
+      nv_frags((t + 1) % 4 == 0 ? rn : rc, (t + 1) % 4, na, nb);
+    else
+      nv_frags(r0, 0, na, nb);
+#pragma unroll
+    for (int q = 0; q < TMW * 4; ++q) {
+      const int i = q / 4, j = q % 4;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < TMW * 4; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if ((t + 1) % 4 == 0 && t < 15) rc = rn;
+#pragma unroll
+    for (int i = 0; i < TMW; ++i) fa[i] = na[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = nb[j];
+  }
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256, 1) void gemm_nvfp4_fast_kernel(FastArgs g) {
+  constexpr int TN = 4, WM = FBM / 2, WN = TN * 32;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // persistent, XCD-aware tile order (as the FP8 kernel)
+  const uint32_t T = (uint32_t)(g.tiles_m * g.tiles_n);
+  const uint32_t G = gridDim.x;
+  const uint32_t xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+  const uint32_t per = T / 8, rem = T % 8;
+  const uint32_t x_begin = xcd * per + (xcd < rem ? xcd : rem);
+  const uint32_t x_end = x_begin + per + (xcd < rem ? 1 : 0);
+  const uint32_t x_wgs = G / 8 + (xcd < G % 8 ? 1 : 0);
+  uint32_t logical = x_begin + local;
+  if (logical >= x_end) return;
+  const uint32_t nk = (uint32_t)(g.K / NV_KT);  // even (checked by the launcher)
+  const uint32_t nsb = (uint32_t)(g.K / 16);    // scale bytes per row
+
+  NvAddr ad;
+  const int h = lane >> 5, x7 = row_swizzle(lane & 31);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) ad.slot[c] = ((2 * c + h) ^ x7) << 4;
+  ad.a_row_off = (wm * WM + (lane & 31)) * FBK;
+  ad.b_row_off = (wn * WN + (lane & 31)) * FBK;
+  ad.a_srow = wm * WM + (lane & 31);
+  ad.b_srow = wn * WN + (lane & 31);
+  ad.sh = 16 * h;
+  const float alpha = *g.ta * *g.tb;
+
+  uint32_t voa[NCHUNK], vob[NCHUNK];
+  chunk_offsets(voa, g.lda);
+  chunk_offsets(vob, g.ldb);
+  const uint32_t vos = (uint32_t)(threadIdx.x * nsb);
+  const uint32_t wl = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
+  auto resources = [&](uint32_t tm0, uint32_t tn0) {
+    TileRes t;
+    t.ra = rows_rsrc(g.a, tm0, g.M, g.lda);
+    t.rb = rows_rsrc(g.b, tn0, g.N, g.ldb);
+    t.rsa = rows_rsrc(g.sa, tm0, g.M, nsb);
+    t.rsb = rows_rsrc(g.sb, tn0, g.N, nsb);
+    return t;
+  };
+
+  uint32_t m0, n0;
+  tile_coords<TN>(g, logical, m0, n0);
+  TileRes cur = resources(m0, n0);
+  nv_issue<0>(cur, voa, vob, vos, wl, 0);
+  nv_issue<1>(cur, voa, vob, vos, wl, 1);
+  wait_vm_lgkm0<NV_FETCHES>();  // stage 0 landed
+  lds_barrier();
+
+  v16f acc[TMW][TN];
+  NvChunk r0;
+  nv_h8 fa[TMW], fb[TN];
+  nv_read_chunk<0>(r0, 0, ad.slot[0], ad.a_row_off, ad.b_row_off, ad.a_srow, ad.b_srow, ad.sh);
+  nv_frags(r0, 0, fa, fb);
+  while (true) {
+    const int64_t cm0 = m0, cn0 = n0;
+    const uint32_t nlogical = logical + x_wgs;
+    const bool more = nlogical < x_end;
+    uint32_t nm0 = m0, nn0 = n0;
+    if (more) tile_coords<TN>(g, nlogical, nm0, nn0);
+    const TileRes nxt_t = resources(nm0, nn0);
+#pragma unroll
+    for (int i = 0; i < TMW; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    // K tiles kt (stage 0) and kt + 1 (stage 1); each refills its stage with
+    // the K tile two ahead, which past the last one is the next tile's
+    // first or second (or this tile's again after the last tile)
+    uint32_t kt = 0;
+    do {
+      nv_ktile<0>(acc, r0, fa, fb, ad, kt + 2 < nk ? cur : nxt_t, kt + 2 < nk ? kt + 2 : kt + 2 - nk, voa, vob, vos, wl);
+      nv_ktile<1>(acc, r0, fa, fb, ad, kt + 3 < nk ? cur : nxt_t, kt + 3 < nk ? kt + 3 : kt + 3 - nk, voa, vob, vos, wl);
+      kt += 2;
+    } while (kt < nk);
+    store_tile<OUT_BF16, TN>(g, acc, alpha, cm0, cn0, wm, wn, lane);
+    if (!more) {
+      wait_vm_lgkm0<0>();  // the repeated fetches land before the workgroup ends
+      break;
+    }
+    logical = nlogical;
+    m0 = nm0;
+    n0 = nn0;
+    cur = nxt_t;
   }
 }
 
@@ -740,6 +989,36 @@ bool launch_scaled_gemm_fast(const uint8_t* a, int fa, bool mx, const void* sa, 
   } else {
     launch(g, 4);
   }
+  return true;
+}
+
+bool launch_gemm_nvfp4_fast(const uint8_t* a, const uint8_t* sa, const float* ta, const uint8_t* b, const uint8_t* sb,
+                            const float* tb, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, void* c,
+                            int c_dtype, int64_t ldc, hipStream_t st) {
+  // eligibility: whole pairs of 256-K tiles, 16-byte rows of codes and of
+  // scale bytes, 32-bit buffer offsets, enough tiles to fill the chip
+  if (K <= 0 || K % (2 * NV_KT) != 0) return false;
+  if ((uintptr_t)a % 16 || (uintptr_t)b % 16 || lda % 16 || ldb % 16) return false;
+  if ((uintptr_t)sa % 16 || (uintptr_t)sb % 16) return false;
+  if (M * lda >= (int64_t)1 << 32 || N * ldb >= (int64_t)1 << 32) return false;
+  if (M * (K / 16) >= (int64_t)1 << 32 || N * (K / 16) >= (int64_t)1 << 32) return false;
+  const int64_t tiles_m = (M + FBM - 1) / FBM, tiles_n = (N + FBN - 1) / FBN;
+  if (tiles_m * tiles_n < 128) return false;
+  FastArgs g{};
+  g.a = a; g.b = b; g.sa = sa; g.sb = sb; g.ta = ta; g.tb = tb;
+  g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.c = c;
+  const bool out_bf16 = (c_dtype == 1);
+  const int esz = out_bf16 ? 2 : 4;
+  g.vec_c = ((uintptr_t)c % 16 == 0) && ((ldc * esz) % 16 == 0);
+  g.tiles_m = tiles_m;
+  g.tiles_n = tiles_n;
+  g.max_wgs = device_cu_count();
+  const int64_t tiles = tiles_m * tiles_n;
+  const unsigned grid = (unsigned)(tiles < g.max_wgs ? tiles : g.max_wgs);
+  if (out_bf16)
+    hipLaunchKernelGGL(gemm_nvfp4_fast_kernel<true>, dim3(grid), dim3(256), 0, st, g);
+  else
+    hipLaunchKernelGGL(gemm_nvfp4_fast_kernel<false>, dim3(grid), dim3(256), 0, st, g);
   return true;
 }
 

@@ -382,6 +382,7 @@ void launch_quantize_nvfp4(const void* x, int dtype, int64_t rows, int64_t cols,
 void launch_gemm_nvfp4(const uint8_t* a, const uint8_t* sa, const float* ta, const uint8_t* b, const uint8_t* sb,
                        const float* tb, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, void* c,
                        int c_dtype, int64_t ldc, hipStream_t stream) {
+  if (launch_gemm_nvfp4_fast(a, sa, ta, b, sb, tb, M, N, K, lda, ldb, c, c_dtype, ldc, stream)) return;
   NvGemmArgs g{};
   g.a = a; g.b = b; g.sa = sa; g.sb = sb; g.ta = ta; g.tb = tb;
   g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.c = c;

@@ -71,6 +71,11 @@ void launch_quantize_nvfp4(const void* x, int dtype, int64_t rows, int64_t cols,
 void launch_gemm_nvfp4(const uint8_t* a, const uint8_t* sa, const float* ta, const uint8_t* b, const uint8_t* sb,
                        const float* tb, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, void* c,
                        int c_dtype, int64_t ldc, hipStream_t st);
+// 256x256 persistent kernel for NVFP4 (f16 MFMA on exactly decoded values);
+// returns false (and launches nothing) when the problem is not eligible.
+bool launch_gemm_nvfp4_fast(const uint8_t* a, const uint8_t* sa, const float* ta, const uint8_t* b, const uint8_t* sb,
+                            const float* tb, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, void* c,
+                            int c_dtype, int64_t ldc, hipStream_t st);
 void launch_scaled_gemm(const uint8_t* a, int fa, int ka, const void* sa, const uint8_t* b, int fb,
                         int kb, const void* sb, int64_t M, int64_t N, int64_t K, int64_t lda,
                         int64_t ldb, void* c, int c_dtype, int64_t ldc, bool accumulate, hipStream_t st);

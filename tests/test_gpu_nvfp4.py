@@ -174,7 +174,9 @@ def tscale(s_dec):
 
 
 GEMM_SHAPES = [(128, 128, 128), (256, 384, 512), (130, 250, 304), (1, 1, 16), (37, 300, 1008),
-               (512, 256, 4096), (64, 64, 16), (100, 200, 48), (257, 129, 80)]
+               (512, 256, 4096), (64, 64, 16), (100, 200, 48), (257, 129, 80),
+               # at least 128 tiles of 256 x 256 and K % 512 == 0: the persistent kernel
+               (4096, 2048, 512), (3968, 2176, 1024)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
@@ -194,7 +196,8 @@ def test_gemm_integer_exact(q, M, N, K):
     assert np.array_equal(gemm(q, *args, out="bf16"), f32_to_bf16_rne_f64(exact))
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (130, 250, 304), (77, 129, 1024), (300, 200, 48)])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (130, 250, 304), (77, 129, 1024), (300, 200, 48),
+                                   (4000, 2100, 1536)])
 def test_gemm_random_codes_wide_scales(q, M, N, K):
     """Any code, any finite non-negative E4M3 block scale (subnormals
     included), tensor scales not powers of two."""

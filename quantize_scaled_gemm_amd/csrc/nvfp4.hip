@@ -40,31 +40,33 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// OCP E4M3 byte -> binary32 (the block scales are non-negative and finite).
+// OCP E4M3 byte -> binary32 (software: the GEMM's general path).
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
   const float v = e == 0 ? (float)m * 0x1p-9f : __builtin_ldexpf((float)(8u + m), (int)e - 10);
   return (c & 0x80u) ? -v : v;
 }
 
-// Saturating RNE E2M1 code of a binary32 value: the nearest of 0, 0.5, 1,
-// 1.5, 2, 3, 4, 6, a midpoint going to the even code; NaN gives sign | 6.
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const uint32_t s = (__float_as_uint(v) >> 28) & 0x8u;
-  const float a = __builtin_fabsf(v);
-  uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
-               (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
-  if (a != a) c = 7u;
-  return s | c;
+// Eight binary32 values times m -> eight E2M1 codes, value i in nibble i.
+// v_cvt_scalef32_pk_fp4_f32 with scale 1 is the saturating RNE encode of the
+// recipe (nearest of 0, 0.5, ..., 6, a midpoint to the even code, the sign
+// of zero kept, NaN to sign | 6); the products are rounded to binary32 first.
+__device__ __forceinline__ uint32_t e2m1x8(float v0, float v1, float v2, float v3, float v4, float v5, float v6,
+                                           float v7, float m) {
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v0 * m, v1 * m, 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v2 * m, v3 * m, 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v4 * m, v5 * m, 1.0f, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v6 * m, v7 * m, 1.0f, 3);
 }
 
 // Block scale code and element multiplier of a block with maximum |x|
-// pattern bmax (non-negative binary32 bits).
+// pattern bmax (non-negative binary32 bits; NaN canonical).  A NaN scale
+// byte decodes to NaN, which gives the multiplier 0 like a zero scale.
 __device__ __forceinline__ void block_scale(uint32_t bmax, float s_enc, uint32_t& code, float& mult) {
   const float sdec = __fdiv_rn(__uint_as_float(bmax), 6.0f);
   code = enc4<kE4M3>(sdec * s_enc, 0.0f, 0.0f, 0.0f) & 0xFFu;
-  const float S = e4m3_to_f32(code);  // 0x7F (NaN block) gives 480 here: excluded below
-  mult = (S > 0.0f && code != 0x7Fu) ? __fdiv_rn(s_enc, S) : 0.0f;
+  const float S = __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+  mult = S > 0.0f ? __fdiv_rn(s_enc, S) : 0.0f;
 }
 
 // ---------------------------------------------------------------------------
@@ -93,31 +95,46 @@ struct NvQuantArgs {
   uint8_t* s;       // rows x cols/16
   uint8_t* qt;      // cols x rows/2, or null
   uint8_t* st;      // cols x rows/16
+  bool qt_vec;      // QT rows of 16-byte aligned runs (qt 16-byte aligned, rows % 32 == 0)
+  bool st_vec;      // 8-byte scale runs aligned (st 8-byte aligned, rows % 128 == 0)
   int64_t tiles_c, ntiles;
 };
 
+// The thread's 8 x 8 values as binary32.  A full tile issues all 16-byte
+// loads before the first use (one wait); a partial tile reads element by
+// element with bounds checks (zeros outside).
 template <typename In>
 __device__ __forceinline__ void load8x8(const NvQuantArgs& a, int64_t r, int64_t c, bool full, float (&v)[8][8]) {
   const In* x = reinterpret_cast<const In*>(a.x);
+  if (full) {
+    constexpr int NV = sizeof(In) == 2 ? 1 : 2;  // 16-byte loads per row
+    u32x4 u[8][NV];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (full) {
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int k = 0; k < NV; ++k) u[j][k] = ld_stream16(x + (r + j) * a.ld + c + 4 * k);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
       if constexpr (sizeof(In) == 2) {
-        const u32x4 u = ld_stream16(x + (r + j) * a.ld + c);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+        const uint32_t w[4] = {u[j][0].x, u[j][0].y, u[j][0].z, u[j][0].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           v[j][2 * k] = bf16lo(w[k]);
           v[j][2 * k + 1] = bf16hi(w[k]);
         }
       } else {
-        const u32x4 u0 = ld_stream16(x + (r + j) * a.ld + c), u1 = ld_stream16(x + (r + j) * a.ld + c + 4);
-        v[j][0] = __uint_as_float(u0.x); v[j][1] = __uint_as_float(u0.y);
-        v[j][2] = __uint_as_float(u0.z); v[j][3] = __uint_as_float(u0.w);
-        v[j][4] = __uint_as_float(u1.x); v[j][5] = __uint_as_float(u1.y);
-        v[j][6] = __uint_as_float(u1.z); v[j][7] = __uint_as_float(u1.w);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+          v[j][4 * k + 0] = __uint_as_float(u[j][k].x);
+          v[j][4 * k + 1] = __uint_as_float(u[j][k].y);
+          v[j][4 * k + 2] = __uint_as_float(u[j][k].z);
+          v[j][4 * k + 3] = __uint_as_float(u[j][k].w);
+        }
       }
-    } else {
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         float f = 0.0f;
@@ -136,8 +153,12 @@ __device__ __forceinline__ void load8x8(const NvQuantArgs& a, int64_t r, int64_t
 __device__ __forceinline__ uint32_t absbits(float f) { return __float_as_uint(f) & 0x7FFFFFFFu; }
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
+constexpr int QT_STRIDE = 17;  // words per column of the LDS tile of column codes
+
 template <typename In>
 __global__ __launch_bounds__(256) void nvfp4_quant_kernel(NvQuantArgs a) {
+  __shared__ uint32_t lds_qt[128 * QT_STRIDE];
+  __shared__ __attribute__((aligned(8))) uint8_t lds_st[128 * 8];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const float s_enc = a.ts[1];
   for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
@@ -157,9 +178,7 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(NvQuantArgs a) {
         uint32_t code;
         float mult;
         block_scale(m > 0x7F800000u ? 0x7FC00000u : m, s_enc, code, mult);
-        uint32_t w = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w |= e2m1_code(v[j][i] * mult) << (4 * i);
+        const uint32_t w = e2m1x8(v[j][0], v[j][1], v[j][2], v[j][3], v[j][4], v[j][5], v[j][6], v[j][7], mult);
         if (r + j < a.rows && c < a.cols) {
           *reinterpret_cast<uint32_t*>(a.q + (r + j) * (a.cols / 2) + c / 2) = w;
           if ((tx & 1) == 0) a.s[(r + j) * (a.cols / 16) + c / 16] = (uint8_t)code;
@@ -167,7 +186,12 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(NvQuantArgs a) {
       }
     }
     if (a.qt) {
-      // column blocks: this lane's 8 rows and its pair row group's (xor 16)
+      // column blocks: this lane's 8 rows and its pair row group's (xor 16).
+      // Inside the matrix the codes go through LDS, [column][64 bytes] with
+      // a 4-byte pad per column, and leave as 16-byte pieces, 4 lanes per
+      // 64-byte run of a QT row; the 8 scale bytes of a column leave as one
+      // 8-byte store.
+      const bool staged = a.qt_vec && r0 + 128 <= a.rows && c0 + 128 <= a.cols;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         uint32_t m = 0;
@@ -177,13 +201,35 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(NvQuantArgs a) {
         uint32_t code;
         float mult;
         block_scale(m > 0x7F800000u ? 0x7FC00000u : m, s_enc, code, mult);
-        uint32_t w = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) w |= e2m1_code(v[j][i] * mult) << (4 * j);
-        if (c + i < a.cols && r < a.rows) {
+        const uint32_t w = e2m1x8(v[0][i], v[1][i], v[2][i], v[3][i], v[4][i], v[5][i], v[6][i], v[7][i], mult);
+        if (staged) {
+          lds_qt[(tx * 8 + i) * QT_STRIDE + ty] = w;
+          if ((ty & 1) == 0) lds_st[(tx * 8 + i) * 8 + (ty >> 1)] = (uint8_t)code;
+        } else if (c + i < a.cols && r < a.rows) {
           *reinterpret_cast<uint32_t*>(a.qt + (c + i) * (a.rows / 2) + r / 2) = w;
           if ((ty & 1) == 0) a.st[(c + i) * (a.rows / 16) + r / 16] = (uint8_t)code;
         }
+      }
+      if (staged) {
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int q = tid + 256 * k, col = q >> 2, part = q & 3;
+          const uint32_t* src = lds_qt + col * QT_STRIDE + part * 4;
+          const u32x4 piece = {src[0], src[1], src[2], src[3]};
+          *reinterpret_cast<u32x4*>(a.qt + (c0 + col) * (a.rows / 2) + r0 / 2 + part * 16) = piece;
+        }
+        if (tid < 128) {
+          const uint2 sc = *reinterpret_cast<const uint2*>(lds_st + tid * 8);
+          uint8_t* dst = a.st + (c0 + tid) * (a.rows / 16) + r0 / 16;
+          if (a.st_vec) {
+            *reinterpret_cast<uint2*>(dst) = sc;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dst[e] = (uint8_t)((e < 4 ? sc.x : sc.y) >> (8 * (e & 3)));
+          }
+        }
+        __syncthreads();  // the LDS tile is reused by the next tile
       }
     }
   }
@@ -369,6 +415,8 @@ void launch_quantize_nvfp4(const void* x, int dtype, int64_t rows, int64_t cols,
   const int esz = dtype == 1 ? 2 : 4;
   a.vec_ok = ((uintptr_t)x % 16 == 0) && ((ld * esz) % 16 == 0);
   a.ts = ts; a.q = q; a.s = s; a.qt = qt; a.st = st;
+  a.qt_vec = qt && ((uintptr_t)qt % 16 == 0) && (rows % 32 == 0);
+  a.st_vec = st && ((uintptr_t)st % 8 == 0) && (rows % 128 == 0);
   a.tiles_c = (cols + 127) / 128;
   a.ntiles = ((rows + 127) / 128) * a.tiles_c;
   int64_t grid = a.ntiles, cap = (int64_t)nv_num_cus() * 8;

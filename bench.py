@@ -21,12 +21,13 @@ before each repetition a 1 GiB scratch buffer is read and written, which
 replaces the 256 MB Infinity Cache, so no operand is served from a previous
 call's cache lines.  The cold pass covers the headline calls (cast + transpose
 of X and dY, the six GEMMs), the other workloads' kernels (tensorwise_256
-latency, delayed_4096, mxfp8_4096, blockwise_7168) and the fp32-master-weight,
+latency, delayed_4096, mxfp8_4096, blockwise_7168, nvfp4_4096) and the fp32-master-weight,
 main-gradient, bf16-wgrad and GeLU kernels, each with its fraction of the
 roofline that bounds it.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R]
                        [--no-cpu-baseline] [--no-workloads]
+       python bench.py --references
        python bench.py --trace-summary DIR --steps K --warmup W
        python bench.py --pmc-summary DIR
 Prints one JSON line on stdout.
@@ -74,14 +75,14 @@ def gemm_flops(m, n, k):
 
 def rate(work, ms, kind):
     """(value, unit, frac) of `work` done in `ms`: kind "hbm" (bytes),
-    "fp8" / "bf16" (flops)."""
+    "fp8" / "bf16" / "f16" (flops)."""
     if ms <= 0:
         return None, None, None
     if kind == "hbm":
         v = work / (ms * 1e-3) / 1e9
         return round(v, 1), "GB/s", round(v / PEAK_HBM_GBPS, 4)
     v = work / (ms * 1e-3) / 1e12
-    peak = PEAK_FP8_TFLOPS if kind == "fp8" else PEAK_BF16_TFLOPS
+    peak = PEAK_FP8_TFLOPS if kind == "fp8" else PEAK_BF16_TFLOPS  # "bf16" / "f16": same dense peak
     return round(v, 1), "TFLOP/s", round(v / peak, 4)
 
 
@@ -393,6 +394,43 @@ def workload_blockwise_7168(torch, q, dev, cold):
     return out
 
 
+def workload_nvfp4_4096(torch, q, dev, cold):
+    """nvfp4_4096: NVFP4 row + column copies of X [16384 x 4096], W [14336 x
+    4096] and dY [16384 x 14336] (2 B in, 2 x (1/2 + 1/16) B out per element;
+    the amax pass that precedes the quantization reads the input a second
+    time and is not counted as algorithmic traffic), and the NVFP4 fprop,
+    dgrad and wgrad (exactly decoded f16 operands: the f16 MFMA peak)."""
+    import workloads
+
+    h = workloads.nvfp4_4096(with_dy=True)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    nv = {}
+    for n in ("X", "W", "dY"):
+        t = dev_bf16(torch, h.pop(n), dev)
+        r, c = t.shape
+        nv[n] = dict(x=t, ts=torch.empty(3, device=dev), q=torch.empty((r, c // 2), **u8),
+                     s=torch.empty((r, c // 16), **u8), qt=torch.empty((c, r // 2), **u8),
+                     st=torch.empty((c, r // 16), **u8))
+    out = {}
+    for n in ("X", "W", "dY"):
+        b = nv[n]
+        out[f"quantize_{n}"] = entry((2.0 + 2 * (0.5 + 1.0 / 16)) * b["x"].numel(), cold.time(
+            lambda b=b: q.qsg_quantize_nvfp4(b["x"], b["ts"], b["q"], b["s"], b["qt"], b["st"])), "hbm")
+    x, w, dy = nv["X"], nv["W"], nv["dY"]
+    Mx, K = x["x"].shape
+    N = w["x"].shape[0]
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    Y, dX, dW = torch.empty((Mx, N), **bf), torch.empty((Mx, K), **bf), torch.empty((N, K), **bf)
+    g = {"fprop": (x["q"], x["s"], x["ts"], w["q"], w["s"], w["ts"], Y),
+         "dgrad": (dy["q"], dy["s"], dy["ts"], w["qt"], w["st"], w["ts"], dX),
+         "wgrad": (dy["qt"], dy["st"], dy["ts"], x["qt"], x["st"], x["ts"], dW)}
+    for k, (a, sa, ta, bb, sb, tb, c) in g.items():
+        out[k] = entry(gemm_flops(a.shape[0], bb.shape[0], 2 * a.shape[1]),
+                       cold.time(lambda a=a, sa=sa, ta=ta, bb=bb, sb=sb, tb=tb, c=c:
+                                 q.qsg_gemm_nvfp4(a, sa, ta, bb, sb, tb, c), reps=5), "f16")
+    return out
+
+
 def workload_extras(torch, q, dev, cold):
     """The rows beyond the four recipes: fp32 master weights -> FP8, the FP8
     wgrad accumulated into an fp32 main gradient, the wgrad kept in bf16, and
@@ -519,6 +557,67 @@ def cpu_baseline(step_flops, step_elems):
 
 
 # ---------------------------------------------------------------------------
+# reference points (library kernels of the same byte mix or GEMM shape; not
+# part of the path, for context only)
+# ---------------------------------------------------------------------------
+def references(torch, dev, reps):
+    """Cold-timed torch / HIP-runtime / hipBLASLt calls with the byte mix of
+    the cast + transpose and the GEMM shapes of linear_4096, so the fractions
+    of the library's kernels can be read against what other kernels reach on
+    the same box."""
+    cold = Cold(torch, dev, reps)
+    out = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    for name, (r, c) in (("32768x4096", (M, H)), ("32768x14336", (M, F))):
+        x = torch.randn((r, c), device=dev, generator=g).to(torch.bfloat16)
+        y = torch.empty_like(x)
+        n = x.numel()
+        out[f"copy_bf16_{name}"] = entry(4.0 * n, cold.time(lambda: y.copy_(x)), "hbm",
+                                         {"what": "torch copy_, bf16 -> bf16 (2 B in, 2 B out)"})
+        f8 = torch.empty((r, c), dtype=torch.float8_e4m3fn, device=dev)
+        out[f"cast_fp8_{name}"] = entry(3.0 * n, cold.time(lambda: f8.copy_(x)), "hbm",
+                                        {"what": "torch copy_ bf16 -> float8_e4m3fn, no scale, no transpose "
+                                                 "(2 B in, 1 B out)"})
+        yt = torch.empty((c, r), dtype=torch.bfloat16, device=dev)
+        out[f"transpose_bf16_{name}"] = entry(4.0 * n, cold.time(lambda: yt.copy_(x.t())), "hbm",
+                                              {"what": "torch copy_ of the transposed view, bf16 (2 B in, 2 B out)"})
+        del x, y, f8, yt
+        torch.cuda.empty_cache()
+    big = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    big2 = torch.empty_like(big)
+    out["copy_1GiB_uint8"] = entry(2.0 * big.numel(), cold.time(lambda: big2.copy_(big)), "hbm",
+                                   {"what": "torch copy_ of 1 GiB (the HIP runtime's device copy)"})
+    del big, big2
+    torch.cuda.empty_cache()
+    # hipBLASLt FP8 GEMM through torch._scaled_mm (bf16 out, per-tensor scales)
+    one = torch.ones((), device=dev)
+    shapes = {"fprop_W": (M, H, H), "fprop_W2": (M, F, H), "dgrad_W2": (M, H, F), "wgrad_W": (H, H, M)}
+    for label, (m, n, k) in shapes.items():
+        try:
+            a = torch.randint(0, 0x7E, (m, k), dtype=torch.uint8, device=dev, generator=g).view(torch.float8_e4m3fn)
+            b = torch.randint(0, 0x7E, (n, k), dtype=torch.uint8, device=dev, generator=g).view(torch.float8_e4m3fn)
+            fn = lambda a=a, b=b: torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+            out[f"hipblaslt_fp8_{label}"] = entry(gemm_flops(m, n, k), cold.time(fn, reps=5), "fp8",
+                                                  {"what": f"torch._scaled_mm E4M3 x E4M3 -> bf16, {m}x{n}x{k}"})
+            del a, b
+        except Exception as e:  # not every torch build exposes it
+            out[f"hipblaslt_fp8_{label}"] = {"error": f"{type(e).__name__}: {e}"[:200]}
+        torch.cuda.empty_cache()
+    # bf16 wgrad dW = dY^T X over 32768 tokens (hipBLASLt through torch.matmul)
+    dy = torch.randn((M, H), device=dev, generator=g).to(torch.bfloat16)
+    xb = torch.randn((M, H), device=dev, generator=g).to(torch.bfloat16)
+    dyt = dy.t().contiguous()
+    out["hipblaslt_bf16_wgrad_W"] = entry(gemm_flops(H, H, M), cold.time(lambda: torch.matmul(dyt, xb), reps=5),
+                                          "bf16", {"what": "torch.matmul(dY^T (contiguous), X), bf16, 4096x4096x32768"})
+    del dy, xb, dyt, cold
+    torch.cuda.empty_cache()
+    out["protocol"] = (f"1 GiB read+write flush before each repetition; median of {reps} repetitions "
+                       f"(GEMMs 5), HIP events on the launch stream")
+    return out
+
+
+# ---------------------------------------------------------------------------
 # rocprofv3 summaries (run on the profiler's output, no GPU needed)
 # ---------------------------------------------------------------------------
 def _read_csvs(pattern):
@@ -541,9 +640,9 @@ def trace_summary(d, steps, warmup):
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     n = steps + warmup
     dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3  # us
-    g4 = [r for r in rows if re.search(r"gemm_fast_kernel<false, [01], 0, true, 4>", r["Kernel_Name"])]
+    g4 = [r for r in rows if re.search(r"gemm_fast_kernel<0, [01], 0, true, 4>", r["Kernel_Name"])]
     tiles = [r for r in rows if "tile_kernel<unsigned short, 0," in r["Kernel_Name"]]
-    tails = [r for r in rows if re.search(r"gemm_fast_kernel<false, 1, 0, true, 2>", r["Kernel_Name"])]
+    tails = [r for r in rows if re.search(r"gemm_fast_kernel<0, 1, 0, true, 2>", r["Kernel_Name"])]
     out = {}
     for i, label in enumerate(GEMM_CALLS):
         seq = [dur(r) for r in g4[i:6 * n:6]][warmup:]
@@ -589,7 +688,7 @@ def pmc_summary(d):
     copies_w = [x for x in write if "copyBuffer" in x[1]]
     ffac = (1 << 30) / (copies_f[-1][2] * 1024.0)
     wfac = (1 << 30) / (copies_w[-1][2] * 1024.0)
-    pat = r"gemm_fast_kernel<false, [01], 0, true, 4>"
+    pat = r"gemm_fast_kernel<0, [01], 0, true, 4>"
     gf = [x for x in fetch if re.search(pat, x[1])]
     gw = [x for x in write if re.search(pat, x[1])]
     res = {"fetch_factor": round(ffac, 4), "write_factor": round(wfac, 4), "calls": {}}
@@ -615,6 +714,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy three times (the reference "
                          "kernel for scaling HBM byte counters)")
+    ap.add_argument("--references", action="store_true",
+                    help="only time reference kernels (torch copies and casts, hipBLASLt GEMMs) and print them")
     ap.add_argument("--trace-summary", metavar="DIR", help="summarise a rocprofv3 kernel trace of this bench")
     ap.add_argument("--pmc-summary", metavar="DIR", help="summarise FETCH_SIZE / WRITE_SIZE counter runs")
     args = ap.parse_args()
@@ -638,6 +739,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     q.load_library()
+
+    if args.references:
+        print(json.dumps(references(torch, dev, args.reps)), flush=True)
+        return
 
     step, step_flops, calls = build_step(torch, q, dev)
 
@@ -730,7 +835,7 @@ def main():
         torch.cuda.empty_cache()
         for name, fn in (("tensorwise_256", workload_tensorwise_256), ("delayed_4096", workload_delayed_4096),
                          ("mxfp8_4096", workload_mxfp8_4096), ("blockwise_7168", workload_blockwise_7168),
-                         ("extras", workload_extras)):
+                         ("nvfp4_4096", workload_nvfp4_4096), ("extras", workload_extras)):
             t2 = time.time()
             line["cold"][name] = fn(torch, q, dev, cold)
             torch.cuda.empty_cache()

@@ -8,25 +8,30 @@
 //
 // Quantization of a block with maximum b, each step one binary32 operation:
 //   sdec = b / 6;  code = E4M3(sdec * s_enc) (saturating RNE);  S = dec(code);
-//   m = s_enc / S (0 when S is 0);  q = E2M1(x * m) (saturating RNE, ties to
-//   the even code).
+//   m = s_enc / S (0 when S is 0 or NaN);  q = E2M1(x * m) (saturating RNE,
+//   ties to the even code).
 // Two codes per byte along the row, element 2i in the low nibble.  The
 // column-wise copy (blocks of 16 rows, stored transposed) shares s_enc.
 //
 // Design for MI355X.
 //   * Quantize: amax pass, a one-thread tensor-scale kernel, then one pass in
-//     128 x 128 tiles (thread = 8 x 8 values, 16-byte loads): a row block is a
-//     lane pair (xor 1), a column block the two row groups of a lane pair
-//     (xor 16), so both copies come from one read of the input.
-//   * GEMM: an NVFP4 value times its block scale has at most 6 significant
-//     bits, so it is exact in bfloat16; operands are decoded to bf16 (block
-//     scale applied) on their way into LDS and multiplied with
-//     v_mfma_f32_32x32x16_bf16, whose 16-K step is exactly one NVFP4 block.
-//     The per-tensor factors s_dec_a * s_dec_b are applied in the epilogue.
-//     (gfx950's FP4 matrix instructions take power-of-two scales per 32
-//     elements, which cannot express an E4M3 scale per 16.)  128 x 128 x 64
-//     tiles, 4 waves of 64 x 64, register-staged: the next K tile's FP4 bytes
-//     are loaded while the current one is multiplied.
+//     128 x 128 tiles (thread = 8 x 8 values, all 16-byte loads of a full tile
+//     in flight together): a row block is a lane pair (xor 1), a column block
+//     the two row groups of a lane pair (xor 16), so both copies come from one
+//     read of the input.  Element codes come from the hardware E2M1
+//     conversion (scale 1), two values per instruction; the column codes
+//     leave through an LDS tile as 16-byte pieces.
+//   * GEMM (this file: the general kernel for any K % 16 == 0 and any
+//     alignment; the persistent 256 x 256 kernel for large aligned problems
+//     is gemm_nvfp4_fast_kernel in gemm_fast.hip): an NVFP4 value times its
+//     block scale has at most 6 significant bits, so it is exact in bfloat16;
+//     operands are decoded to bf16 (block scale applied) on their way into LDS
+//     and multiplied with v_mfma_f32_32x32x16_bf16, whose 16-K step is exactly
+//     one NVFP4 block.  The per-tensor factors s_dec_a * s_dec_b are applied
+//     in the epilogue.  (gfx950's FP4 matrix instructions take power-of-two
+//     scales per 32 elements, which cannot express an E4M3 scale per 16.)
+//     128 x 128 x 64 tiles, 4 waves of 64 x 64, register-staged: the next K
+//     tile's FP4 bytes are loaded while the current one is multiplied.
 #include <hip/hip_runtime.h>
 
 #include "qsg_device.h"

@@ -238,9 +238,26 @@ __global__ __launch_bounds__(NTH, 1) void gemm_block2_kernel(Block2Args g) {
 #pragma unroll
       for (int j = 0; j < TJ; ++j) acc[i][j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
+    // The partial sums of the previous B fragment (pp) and their scale
+    // factors (pfa: A-row factors of their K tile; pfb: their B factors) are
+    // promoted while the next fragment's MFMAs run: MFMA i of fragment j is
+    // followed by the 4 fmas of pp[i], which read results 4 MFMAs old, so no
+    // fma waits on the matrix core and the VALU work issues in the MFMAs'
+    // shadow.  The first promotion of a tile adds 0 * 0.
+    v4f pp[TI];
+    float pfa[TI], pfb[4];
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      pp[i] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+      pfa[i] = 0.0f;
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) pfb[v] = 0.0f;
+
     // K tile KT in stage S; its scales are word KI of group buffer GB.
     //   1. scale factors and the 4 A fragments; the 8 B fragments one ahead
-    //      of their 4 MFMAs, each MFMA's result promoted right after it;
+    //      of their 4 MFMAs; the previous fragment's partial sums promoted
+    //      between them;
     //   2. after the last fragment read: barrier, then the fetch of K tile
     //      KT + 2 into S (and, at KI == 1, the next scale group);
     //   3. wait for this wave's fetches of KT + 1, barrier.
@@ -257,25 +274,34 @@ __global__ __launch_bounds__(NTH, 1) void gemm_block2_kernel(Block2Args g) {
       v8i bn = bf;                                                                                         \
       if (j + 1 < TJ) bn = frag16(st_b<S>(), b_off + (j + 1) * 16 * BK, c_lo, c_hi);                       \
       float fbv[4];                                                                                        \
-      if constexpr (!W128) {                                                                               \
+      if constexpr (W128) {                                                                                \
+        _Pragma("unroll") for (int v = 0; v < 4; ++v) fbv[v] = fb_w;                                       \
+      } else {                                                                                             \
         _Pragma("unroll") for (int v = 0; v < 4; ++v)                                                      \
           fbv[v] = gr_sb<GB>()[sb_idx + (j * 16 + v) * GROUP + (KI)];                                      \
       }                                                                                                    \
-      /* the 4 partial sums of this B fragment first, then their promotion: */                           \
-      /* the fmas of one MFMA wait for it while the next MFMAs issue */                                    \
       v4f part[TI];                                                                                        \
-      _Pragma("unroll") for (int i = 0; i < TI; ++i)                                                       \
+      _Pragma("unroll") for (int i = 0; i < TI; ++i) {                                                     \
         part[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[i], (v4f){0.0f, 0.0f, 0.0f, 0.0f}, \
                                                                    FB, FA, 0, 0, 0, 0);                    \
-      _Pragma("unroll") for (int i = 0; i < TI; ++i) {                                                     \
         if constexpr (W128) {                                                                              \
-          const float f = fa_[i] * fb_w;                                                                   \
-          _Pragma("unroll") for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(part[i][v], f, acc[i][j][v]); \
+          const float f = pfa[i] * pfb[0];                                                                 \
+          _Pragma("unroll") for (int v = 0; v < 4; ++v) acc[i][(j + TJ - 1) % TJ][v] = __builtin_fmaf(pp[i][v], f, acc[i][(j + TJ - 1) % TJ][v]); \
         } else {                                                                                           \
           _Pragma("unroll") for (int v = 0; v < 4; ++v)                                                    \
-            acc[i][j][v] = __builtin_fmaf(part[i][v], fa_[i] * fbv[v], acc[i][j][v]);                       \
+            acc[i][(j + TJ - 1) % TJ][v] = __builtin_fmaf(pp[i][v], pfa[i] * pfb[v], acc[i][(j + TJ - 1) % TJ][v]);                    \
         }                                                                                                  \
       }                                                                                                    \
+      _Pragma("unroll") for (int q = 0; q < TI; ++q) {                                                     \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                 \
+        __builtin_amdgcn_sched_group_barrier(0x002, W128 ? 5 : 8, 0);                                      \
+      }                                                                                                    \
+      __builtin_amdgcn_sched_barrier(0);                                                                   \
+      _Pragma("unroll") for (int i = 0; i < TI; ++i) {                                                     \
+        pp[i] = part[i];                                                                                   \
+        pfa[i] = fa_[i];                                                                                   \
+      }                                                                                                    \
+      _Pragma("unroll") for (int v = 0; v < 4; ++v) pfb[v] = fbv[v];                                       \
       bf = bn;                                                                                             \
       if (j == TJ - 2) {                                                                                   \
         /* every fragment of stage S is read: release it for K tile KT + 2 */                              \
@@ -312,6 +338,11 @@ __global__ __launch_bounds__(NTH, 1) void gemm_block2_kernel(Block2Args g) {
       kt += 8;
     } while (kt < nk);
 #undef QSG_B2_STEP
+    // the last fragment's partial sums
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[i][TJ - 1][v] = __builtin_fmaf(pp[i][v], pfa[i] * pfb[v], acc[i][TJ - 1][v]);
 
     // ---- epilogue: lane l of tile (i, j) holds row 16 i + l % 16 and the 4
     // columns 16 j + 4 (l / 16) .. + 3 of the wave's block ----

@@ -184,6 +184,9 @@ __global__ __launch_bounds__(NTH, 1) void gemm_block2_kernel(Block2Args g) {
   if (logical >= x_end) return;
   const uint32_t nk = (uint32_t)(g.K / BK);  // a multiple of 8 (checked by the launcher)
   const uint32_t ngrp = nk / GROUP;
+  // B fragments are read PF fragments ahead of their MFMAs (the 1 x 128
+  // layout holds 4 more scale factors per fragment and has no room for 2)
+  constexpr int PF = W128 ? 2 : 1;
   const int64_t sstride = (g.K / BK) * 4;   // bytes per scale row
 
   // fragment addressing
@@ -270,9 +273,11 @@ __global__ __launch_bounds__(NTH, 1) void gemm_block2_kernel(Block2Args g) {
     v8i af[TI];                                                                                            \
     _Pragma("unroll") for (int i = 0; i < TI; ++i) af[i] = frag16(st_a<S>(), a_off + i * 16 * BK, c_lo, c_hi); \
     v8i bf = frag16(st_b<S>(), b_off, c_lo, c_hi);                                                         \
+    v8i bn = bf;                                                                                           \
+    if constexpr (PF == 2) bn = frag16(st_b<S>(), b_off + 16 * BK, c_lo, c_hi);                             \
     _Pragma("unroll") for (int j = 0; j < TJ; ++j) {                                                       \
-      v8i bn = bf;                                                                                         \
-      if (j + 1 < TJ) bn = frag16(st_b<S>(), b_off + (j + 1) * 16 * BK, c_lo, c_hi);                       \
+      v8i bnn = bn;                                                                                        \
+      if (j + PF < TJ) bnn = frag16(st_b<S>(), b_off + (j + PF) * 16 * BK, c_lo, c_hi);                    \
       float fbv[4];                                                                                        \
       if constexpr (W128) {                                                                                \
         _Pragma("unroll") for (int v = 0; v < 4; ++v) fbv[v] = fb_w;                                       \
@@ -302,8 +307,13 @@ __global__ __launch_bounds__(NTH, 1) void gemm_block2_kernel(Block2Args g) {
         pfa[i] = fa_[i];                                                                                   \
       }                                                                                                    \
       _Pragma("unroll") for (int v = 0; v < 4; ++v) pfb[v] = fbv[v];                                       \
-      bf = bn;                                                                                             \
-      if (j == TJ - 2) {                                                                                   \
+      if constexpr (PF == 2) {                                                                             \
+        bf = bn;                                                                                           \
+        bn = bnn;                                                                                          \
+      } else {                                                                                             \
+        bf = bnn;                                                                                          \
+      }                                                                                                    \
+      if (j == TJ - 1 - PF) {                                                                              \
         /* every fragment of stage S is read: release it for K tile KT + 2 */                              \
         wait_vm_lgkm0<63>();                                                                               \
         lds_barrier();                                                                                     \

@@ -121,6 +121,14 @@ __device__ __forceinline__ void issue_tile(const Res& r, const uint32_t (&voa)[N
   for (int i = 0; i < NCK; ++i) dma16(r.rb, vob[i], kt * BK, st_b<S>() + i * NW * 1024 + wl);
 }
 
+// Load q (0 .. NCK-1) of the A tile and of the B tile of K tile kt.
+template <int S>
+__device__ __forceinline__ void issue_pair(const Res& r, const uint32_t (&voa)[NCK], const uint32_t (&vob)[NCK],
+                                           uint32_t wl, uint32_t kt, int q) {
+  dma16(r.ra, voa[q], kt * BK, st_a<S>() + q * NW * 1024 + wl);
+  dma16(r.rb, vob[q], kt * BK, st_b<S>() + q * NW * 1024 + wl);
+}
+
 // Scale group g: waves 0-3 the A rows' 16 bytes, waves 4-7 the B side's.
 template <int G>
 __device__ __forceinline__ void issue_group(const Res& r, uint32_t vos, uint32_t wl, uint32_t g) {
@@ -187,6 +195,13 @@ __global__ __launch_bounds__(NTH, 1) void gemm_block2_kernel(Block2Args g) {
   // B fragments are read PF fragments ahead of their MFMAs (the 1 x 128
   // layout holds 4 more scale factors per fragment and has no room for 2)
   constexpr int PF = W128 ? 2 : 1;
+  // Fetch schedule.  ONEBAR (1 x 128 layout): one barrier per K tile; the
+  // next K tile goes into the other stage during the first half of this one
+  // (two loads per fragment).  Otherwise two barriers per K tile: stage S is
+  // released once its last fragment is read and refilled at once with the K
+  // tile two ahead, which gives the loads more than a K tile to land (the
+  // weight-block fprop, whose output is the largest, loses 5 % without that).
+  constexpr bool ONEBAR = !W128;
   const int64_t sstride = (g.K / BK) * 4;   // bytes per scale row
 
   // fragment addressing
@@ -222,11 +237,14 @@ __global__ __launch_bounds__(NTH, 1) void gemm_block2_kernel(Block2Args g) {
   uint32_t m0, n0;
   tile_coords<0>(g, logical, m0, n0);
   Res cur = resources(m0, n0);
-  constexpr int NF = 2 * NCK;  // fetches of one K tile
   issue_group<0>(cur, vos, wl, 0);
   issue_tile<0>(cur, voa, vob, wl, 0);
-  issue_tile<1>(cur, voa, vob, wl, 1);
-  wait_vm_lgkm0<NF>();  // group 0 and K tile 0 landed (this wave's part)
+  if constexpr (ONEBAR) {
+    wait_vm_lgkm0<0>();  // group 0 and K tile 0 landed (this wave's part)
+  } else {
+    issue_tile<1>(cur, voa, vob, wl, 1);
+    wait_vm_lgkm0<2 * NCK>();
+  }
   lds_barrier();
 
   v4f acc[TI][TJ];
@@ -313,7 +331,25 @@ __global__ __launch_bounds__(NTH, 1) void gemm_block2_kernel(Block2Args g) {
       } else {                                                                                             \
         bf = bnn;                                                                                          \
       }                                                                                                    \
-      if (j == TJ - 1 - PF) {                                                                              \
+      if constexpr (ONEBAR) {                                                                              \
+        if (j < NCK) {                                                                                     \
+          /* the next K tile into the other stage, one pair of loads per fragment */                        \
+          const bool own = (KT) + 1 < nk;                                                                  \
+          Res RES = own ? cur : nxt;                                                                       \
+          uint32_t FK = own ? (KT) + 1 : 0;                                                                \
+          asm volatile("" : "+s"(RES.ra), "+s"(RES.rb), "+s"(FK));                                         \
+          issue_pair<(S) ^ 1>(RES, voa, vob, wl, FK, j);                                                   \
+          if constexpr ((KI) == 1) {                                                                       \
+            if (j == 0) {                                                                                  \
+              const uint32_t ng = (KT) / GROUP + 1;                                                        \
+              const bool sown = ng < ngrp;                                                                 \
+              Res SR = sown ? cur : nxt;                                                                   \
+              uint32_t SG = sown ? ng : 0;                                                                 \
+              issue_group<(GB) ^ 1>(SR, vos, wl, SG);                                                      \
+            }                                                                                              \
+          }                                                                                                \
+        }                                                                                                  \
+      } else if (j == TJ - 1 - PF) {                                                                       \
         /* every fragment of stage S is read: release it for K tile KT + 2 */                              \
         wait_vm_lgkm0<63>();                                                                               \
         lds_barrier();                                                                                     \
@@ -331,7 +367,10 @@ __global__ __launch_bounds__(NTH, 1) void gemm_block2_kernel(Block2Args g) {
         }                                                                                                  \
       }                                                                                                    \
     }                                                                                                      \
-    wait_vm_lgkm0<((KI) == 1 ? NF + 1 : NF)>();                                                            \
+    if constexpr (ONEBAR)                                                                                  \
+      wait_vm_lgkm0<0>();                                                                                  \
+    else                                                                                                   \
+      wait_vm_lgkm0<((KI) == 1 ? 2 * NCK + 1 : 2 * NCK)>();                                                \
     lds_barrier();                                                                                         \
   }
 

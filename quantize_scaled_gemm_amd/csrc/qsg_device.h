@@ -81,6 +81,21 @@ __device__ __forceinline__ uint32_t enc4(float a, float b, float c, float d) {
   return cvt_pk<FMT, true>(c, d, lo);
 }
 
+// Four binary32 values known to be finite with |v| <= max (no clamp, no NaN
+// patch needed): the hardware RNE conversion alone gives enc().
+template <int FMT>
+__device__ __forceinline__ uint32_t enc4_inrange(float a, float b, float c, float d) {
+  uint32_t r;
+  if constexpr (FMT == kE4M3) {
+    r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)r, true);
+  } else {
+    r = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    r = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c, d, (int)r, true);
+  }
+  return r;
+}
+
 // bf16 <-> fp32 (exact widening; RNE narrowing of finite values, NaN kept quiet).
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

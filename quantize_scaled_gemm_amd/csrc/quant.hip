@@ -358,6 +358,10 @@ __global__ __launch_bounds__(256) void tile_kernel(TileArgs a) {
     // ---- scales -----------------------------------------------------------
     float rs[8];  // row-wise multiplier for each of this thread's rows
     float cs[8];  // column-wise multiplier for each of this thread's columns
+    // MXFP8 with the CEIL exponent rule on blocks with no infinity or NaN:
+    // every scaled value is exactly <= max (a power-of-two scale), so the
+    // encode needs no clamp and no NaN patch
+    bool inrange = false;
     if constexpr (MODE == MODE_TENSOR) {
       uint32_t m = 0;
 #pragma unroll
@@ -385,6 +389,10 @@ __global__ __launch_bounds__(256) void tile_kernel(TileArgs a) {
         colmax[i] = group_max_u32<0x30>(m);  // the 4 row groups of this wave
       }
       if constexpr (MODE == MODE_MX) {
+        uint32_t mm = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) mm = umax(mm, umax(rowmax[k], colmax[k]));
+        inrange = a.mx_ceil && mm < 0x7F800000u;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           int e = mx_exponent(rowmax[j], EMAX, a.mx_ceil, a.margin);
@@ -452,11 +460,20 @@ __global__ __launch_bounds__(256) void tile_kernel(TileArgs a) {
     constexpr bool SAME_SCALE = (MODE == MODE_TENSOR || MODE == MODE_B128X128);
     uint32_t rq[8][2];
     if (SAME_SCALE || a.q) {
+      if (MODE == MODE_MX && inrange) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float s = rs[j];
-        rq[j][0] = enc4<FMT>(b.at(j, 0) * s, b.at(j, 1) * s, b.at(j, 2) * s, b.at(j, 3) * s);
-        rq[j][1] = enc4<FMT>(b.at(j, 4) * s, b.at(j, 5) * s, b.at(j, 6) * s, b.at(j, 7) * s);
+        for (int j = 0; j < 8; ++j) {
+          const float s = rs[j];
+          rq[j][0] = enc4_inrange<FMT>(b.at(j, 0) * s, b.at(j, 1) * s, b.at(j, 2) * s, b.at(j, 3) * s);
+          rq[j][1] = enc4_inrange<FMT>(b.at(j, 4) * s, b.at(j, 5) * s, b.at(j, 6) * s, b.at(j, 7) * s);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float s = rs[j];
+          rq[j][0] = enc4<FMT>(b.at(j, 0) * s, b.at(j, 1) * s, b.at(j, 2) * s, b.at(j, 3) * s);
+          rq[j][1] = enc4<FMT>(b.at(j, 4) * s, b.at(j, 5) * s, b.at(j, 6) * s, b.at(j, 7) * s);
+        }
       }
     }
     if (a.q) {
@@ -480,6 +497,13 @@ __global__ __launch_bounds__(256) void tile_kernel(TileArgs a) {
         transpose4x4_bytes(rq[4][0], rq[5][0], rq[6][0], rq[7][0], cq[0][1], cq[1][1], cq[2][1], cq[3][1]);
         transpose4x4_bytes(rq[0][1], rq[1][1], rq[2][1], rq[3][1], cq[4][0], cq[5][0], cq[6][0], cq[7][0]);
         transpose4x4_bytes(rq[4][1], rq[5][1], rq[6][1], rq[7][1], cq[4][1], cq[5][1], cq[6][1], cq[7][1]);
+      } else if (MODE == MODE_MX && inrange) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float s = cs[i];
+          cq[i][0] = enc4_inrange<FMT>(b.at(0, i) * s, b.at(1, i) * s, b.at(2, i) * s, b.at(3, i) * s);
+          cq[i][1] = enc4_inrange<FMT>(b.at(4, i) * s, b.at(5, i) * s, b.at(6, i) * s, b.at(7, i) * s);
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {

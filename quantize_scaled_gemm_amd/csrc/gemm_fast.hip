@@ -253,10 +253,14 @@ __device__ __forceinline__ void load_frags(Frags<TN>& f, int kk, int a_row_off, 
 #pragma unroll
   for (int j = 0; j < TN; ++j) f.b[j] = ffrag(stage_b<S>(), b_row_off, j, c_lo, c_hi);
   if constexpr (SC == SC_MXG) {
+    // step 0 only: the word shifted by 8h serves both 64-K steps (op_sel 0
+    // and 2 pick bytes h and 2 + h); step 1 copies it (mfma_range<..., 2>)
+    if (kk == 0) {
 #pragma unroll
-    for (int i = 0; i < TMW; ++i) f.sa[i] = (int)(group_sa<GB>()[(a_srow + i * 32) * 4 + KI] >> sh);
+      for (int i = 0; i < TMW; ++i) f.sa[i] = (int)(group_sa<GB>()[(a_srow + i * 32) * 4 + KI] >> sh);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) f.sb[j] = (int)(group_sb<GB>()[(b_srow + j * 32) * 4 + KI] >> sh);
+      for (int j = 0; j < TN; ++j) f.sb[j] = (int)(group_sb<GB>()[(b_srow + j * 32) * 4 + KI] >> sh);
+    }
   } else if constexpr (SC == SC_MX) {
 #pragma unroll
     for (int i = 0; i < TMW; ++i) f.sa[i] = (int)(stage_sa<S>()[a_srow + i * 32] >> sh);
@@ -266,14 +270,14 @@ __device__ __forceinline__ void load_frags(Frags<TN>& f, int kk, int a_row_off, 
 }
 
 // MFMAs LO..HI-1 of one 64-K step, MFMA q updating accumulator tile
-// (q / TN, q % TN).
-template <bool MX, int FA, int FB, int LO, int HI, int TN>
+// (q / TN, q % TN); OPS: the byte of the scale words (op_sel).
+template <bool MX, int FA, int FB, int LO, int HI, int TN, int OPS = 0>
 __device__ __forceinline__ void mfma_range(v16f (&acc)[TMW][TN], const Frags<TN>& f) {
 #pragma unroll
   for (int q = LO; q < HI; ++q) {
     const int i = q / TN, j = q % TN;
     if constexpr (MX)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, 0, f.sb[j], 0, f.sa[i]);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, OPS, f.sb[j], OPS, f.sa[i]);
     else
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, 0, 0, 0, 0);
   }
@@ -499,6 +503,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
   const int a_srow = wm * WM + (lane & 31), b_srow = wn * WN + (lane & 31);
   // MX: bytes h (first 64-K step) and 2 + h (second) of the row's word
   const int sh0 = 8 * h, sh1 = 8 * h + 16;
+  constexpr int OPS1 = SC == SC_MXG ? 2 : 0;  // scale byte of the second 64-K step
   float alpha = 1.0f;
   if constexpr (!MX) alpha = *reinterpret_cast<const float*>(g.sa) * *reinterpret_cast<const float*>(g.sb);
 
@@ -569,6 +574,10 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     constexpr bool SGF = SC == SC_MXG && (KI) == 1;  /* this step fetches the next scale group */ \
     constexpr int NAS = NA + (SGF ? 2 : 0);                                                    \
     load_frags<S, SC, GB, KI, TN>(f1, 1, a_row_off, b_row_off, c10, c11, a_srow, b_srow, sh1); \
+    if constexpr (SC == SC_MXG) {                                                              \
+      _Pragma("unroll") for (int i = 0; i < TMW; ++i) f1.sa[i] = f0.sa[i];                     \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j) f1.sb[j] = f0.sb[j];                      \
+    }                                                                                          \
     mfma_range<MX, FA, FB, 0, P1>(acc, f0);                                                    \
     _Pragma("unroll") for (int q = 0; q < P1 - 1; ++q) {                                       \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
@@ -589,7 +598,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
       issue_scale_group<(GB) ^ 1>(SRES, vos, wl, SG);                                          \
     }                                                                                          \
     mfma_range<MX, FA, FB, P1, NQ>(acc, f0);                                                   \
-    mfma_range<MX, FA, FB, 0, P2>(acc, f1);                                                    \
+    mfma_range<MX, FA, FB, 0, P2, TN, OPS1>(acc, f1);                                          \
     _Pragma("unroll") for (int q = 0; q < (NAS < NQ - P1 + P2 ? NAS : NQ - P1 + P2); ++q) {    \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);                                       \
       __builtin_amdgcn_sched_group_barrier(0x001, 3, 1);                                       \
@@ -602,7 +611,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     load_frags<S ^ 1, SC, ((KI) == 3 ? (GB) ^ 1 : (GB)), (((KI) + 1) & 3), TN>(                \
         f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);                           \
     issue_part<S, 1, SC, TN>(RES, voa, vob, vos, wl, FK);                                      \
-    mfma_range<MX, FA, FB, P2, NQ>(acc, f1);                                                   \
+    mfma_range<MX, FA, FB, P2, NQ, TN, OPS1>(acc, f1);                                         \
     _Pragma("unroll") for (int q = 0; q < NQ - P2 - 1; ++q) {                                  \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);                                       \
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TMW + TN) / (NQ - P2 - 1), 2);          \

@@ -248,10 +248,6 @@ __device__ __forceinline__ void lds_barrier() {
 template <int S, int SC, int GB, int KI, int TN>
 __device__ __forceinline__ void load_frags(Frags<TN>& f, int kk, int a_row_off, int b_row_off, int c_lo, int c_hi,
                                            int a_srow, int b_srow, int sh) {
-#pragma unroll
-  for (int i = 0; i < TMW; ++i) f.a[i] = ffrag(stage_a<S>(), a_row_off, i, c_lo, c_hi);
-#pragma unroll
-  for (int j = 0; j < TN; ++j) f.b[j] = ffrag(stage_b<S>(), b_row_off, j, c_lo, c_hi);
   if constexpr (SC == SC_MXG) {
     // step 0 only: the word shifted by 8h serves both 64-K steps (op_sel 0
     // and 2 pick bytes h and 2 + h); step 1 copies it (mfma_range<..., 2>)
@@ -267,6 +263,11 @@ __device__ __forceinline__ void load_frags(Frags<TN>& f, int kk, int a_row_off, 
 #pragma unroll
     for (int j = 0; j < TN; ++j) f.sb[j] = (int)(stage_sb<S>()[b_srow + j * 32] >> sh);
   }
+  // the scale words first: the first MFMA needs them and the LDS returns reads in order
+#pragma unroll
+  for (int i = 0; i < TMW; ++i) f.a[i] = ffrag(stage_a<S>(), a_row_off, i, c_lo, c_hi);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) f.b[j] = ffrag(stage_b<S>(), b_row_off, j, c_lo, c_hi);
 }
 
 // MFMAs LO..HI-1 of one 64-K step, MFMA q updating accumulator tile

@@ -309,23 +309,28 @@ __device__ __forceinline__ void delayed_finish(const TileArgs& a, uint32_t m, fl
       last = (n == ngrp - 1) ? 1u : 0u;
     }
     red[4] = last;
-    if (last) {
-      uint32_t am = 0;
-      for (uint32_t i = 0; i < ngrp; ++i) {
-        const uint32_t v = __hip_atomic_load(a.ws + i * WS_LINE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        am = am > v ? am : v;
-      }
-      for (uint32_t i = 0; i < ngrp; ++i) {
-        __hip_atomic_store(a.ws + i * WS_LINE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(a.ws + i * WS_LINE + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      __hip_atomic_store(a.ws + DELAYED_GROUPS * WS_LINE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (a.amax_out) *a.amax_out = am;
-      red[5] = am;
-    }
   }
   __syncthreads();
-  if (red[4]) history_update_wg(a.hist, a.hist_len, a.slot, red[5], fmax, a.margin, a.scale_w, a.scale_inv_w, red + 8);
+  if (red[4]) {
+    // the last workgroup: one lane per group reads and clears its line
+    const uint32_t G = gridDim.x;
+    const uint32_t ngrp = G < DELAYED_GROUPS ? G : DELAYED_GROUPS;
+    uint32_t v = 0;
+    if (threadIdx.x < ngrp) {
+      uint32_t* line = a.ws + threadIdx.x * WS_LINE;
+      v = __hip_atomic_load(line, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(line, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(line + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    v = wave_max_u32(v);  // the group lanes are all in wave 0
+    if (threadIdx.x == 0) {
+      __hip_atomic_store(a.ws + DELAYED_GROUPS * WS_LINE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (a.amax_out) *a.amax_out = v;
+      red[5] = v;
+    }
+    __syncthreads();
+    history_update_wg(a.hist, a.hist_len, a.slot, red[5], fmax, a.margin, a.scale_w, a.scale_inv_w, red + 8);
+  }
 }
 
 template <typename In, int MODE, int FMT>
@@ -563,9 +568,13 @@ int num_cus() {
 
 template <typename In, int MODE>
 void launch_tile(const TileArgs& a, int fmt, hipStream_t st) {
-  // persistent grid: enough workgroups for several waves per SIMD
+  // persistent grid: enough workgroups for several waves per SIMD.  The
+  // per-tensor cast takes 2 per CU: its fused amax ends in one device-scope
+  // atomic per workgroup on one address, which the memory side performs one
+  // at a time (with 8 per CU a 64 MB tensor spent more time on them than on
+  // its bytes), and it streams as fast with 2
   int64_t grid = a.ntiles;
-  const int64_t cap = (int64_t)num_cus() * 8;
+  const int64_t cap = (int64_t)num_cus() * (MODE == MODE_TENSOR ? 2 : 8);
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
   if (fmt == kE4M3)

@@ -197,11 +197,11 @@ ActArgs act_args(const void* x, int64_t rows, int64_t cols, int64_t ld, const fl
   return g;
 }
 
-// (chunks of a row over x, rows over y), at most 8 workgroups per CU in all
-dim3 act_grid(const ActArgs& g) {
+// (chunks of a row over x, rows over y), at most per_cu workgroups per CU in all
+dim3 act_grid(const ActArgs& g, int per_cu) {
   const int64_t cv = g.vec_ok ? g.cols / 8 : 0;
   const int64_t per_row = cv + (g.cols - cv * 8);
-  const int64_t cap = (int64_t)num_cus_act() * 8;
+  const int64_t cap = (int64_t)num_cus_act() * per_cu;
   int64_t gx = (per_row + 255) / 256;
   if (gx > cap) gx = cap;
   if (gx < 1) gx = 1;
@@ -220,7 +220,9 @@ void launch_act_fp8_store_fwd(const void* h, int64_t rows, int64_t cols, int64_t
   if (rows == 0 || cols == 0) return;
   ActArgs g = act_args(h, rows, cols, ld, scale, q, a);
   g.amax_out = reinterpret_cast<uint32_t*>(amax_out);
-  const dim3 grid = act_grid(g);
+  // with the fused amax every workgroup ends in an atomic on one address,
+  // which the memory side performs one at a time: fewer workgroups then
+  const dim3 grid = act_grid(g, amax_out ? 2 : 8);
   if (fmt == kE4M3)
     hipLaunchKernelGGL(act_fwd_kernel<kE4M3>, grid, dim3(256), 0, st, g);
   else
@@ -231,7 +233,7 @@ void launch_act_fp8_store_bwd(const void* da, int64_t rows, int64_t cols, int64_
                               const float* scale_inv, void* dh, hipStream_t st) {
   if (rows == 0 || cols == 0) return;
   const ActArgs g = act_args(da, rows, cols, ld, scale_inv, const_cast<uint8_t*>(q), dh);
-  const dim3 grid = act_grid(g);
+  const dim3 grid = act_grid(g, 8);
   if (fmt == kE4M3)
     hipLaunchKernelGGL(act_bwd_kernel<kE4M3>, grid, dim3(256), 0, st, g);
   else

@@ -64,14 +64,21 @@ __device__ __forceinline__ uint32_t e2m1x8(float v0, float v1, float v2, float v
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v6 * m, v7 * m, 1.0f, 3);
 }
 
-// Block scale code and element multiplier of a block with maximum |x|
-// pattern bmax (non-negative binary32 bits; NaN canonical).  A NaN scale
-// byte decodes to NaN, which gives the multiplier 0 like a zero scale.
-__device__ __forceinline__ void block_scale(uint32_t bmax, float s_enc, uint32_t& code, float& mult) {
-  const float sdec = __fdiv_rn(__uint_as_float(bmax), 6.0f);
-  code = enc4<kE4M3>(sdec * s_enc, 0.0f, 0.0f, 0.0f) & 0xFFu;
+// Element multiplier of an E4M3 block-scale code: fp32(s_enc / S), 0 when S
+// is 0 or NaN (code 0x7F; a NaN block).  The codes of the non-negative block
+// scales are 0..127, so a workgroup tabulates the 128 quotients once.
+__device__ __forceinline__ float mult_of_code(uint32_t code, float s_enc) {
   const float S = __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
-  mult = S > 0.0f ? __fdiv_rn(s_enc, S) : 0.0f;
+  return S > 0.0f ? __fdiv_rn(s_enc, S) : 0.0f;
+}
+
+// Block scale code of a block with maximum |x| pattern bmax (non-negative
+// binary32 bits; NaN canonical) and its element multiplier from the table.
+__device__ __forceinline__ void block_scale(uint32_t bmax, float s_enc, const float* mult_table, uint32_t& code,
+                                            float& mult) {
+  const float sdec = __fdiv_rn(__uint_as_float(bmax), 6.0f);
+  code = cvt_pk<kE4M3, false>(sdec * s_enc, 0.0f, 0u) & 0xFFu;
+  mult = mult_table[code & 0x7Fu];
 }
 
 // ---------------------------------------------------------------------------
@@ -164,8 +171,11 @@ template <typename In>
 __global__ __launch_bounds__(256) void nvfp4_quant_kernel(NvQuantArgs a) {
   __shared__ uint32_t lds_qt[128 * QT_STRIDE];
   __shared__ __attribute__((aligned(8))) uint8_t lds_st[128 * 8];
+  __shared__ float lds_mult[128];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const float s_enc = a.ts[1];
+  if (tid < 128) lds_mult[tid] = mult_of_code((uint32_t)tid, s_enc);
+  __syncthreads();
   for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
     const int64_t r0 = (tile / a.tiles_c) * 128, c0 = (tile % a.tiles_c) * 128;
     const int64_t r = r0 + ty * 8, c = c0 + tx * 8;
@@ -182,7 +192,7 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(NvQuantArgs a) {
         m = umax(m, (uint32_t)__shfl_xor((int)m, 1, 64));
         uint32_t code;
         float mult;
-        block_scale(m > 0x7F800000u ? 0x7FC00000u : m, s_enc, code, mult);
+        block_scale(m > 0x7F800000u ? 0x7FC00000u : m, s_enc, lds_mult, code, mult);
         const uint32_t w = e2m1x8(v[j][0], v[j][1], v[j][2], v[j][3], v[j][4], v[j][5], v[j][6], v[j][7], mult);
         if (r + j < a.rows && c < a.cols) {
           *reinterpret_cast<uint32_t*>(a.q + (r + j) * (a.cols / 2) + c / 2) = w;
@@ -205,7 +215,7 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(NvQuantArgs a) {
         m = umax(m, (uint32_t)__shfl_xor((int)m, 16, 64));
         uint32_t code;
         float mult;
-        block_scale(m > 0x7F800000u ? 0x7FC00000u : m, s_enc, code, mult);
+        block_scale(m > 0x7F800000u ? 0x7FC00000u : m, s_enc, lds_mult, code, mult);
         const uint32_t w = e2m1x8(v[0][i], v[1][i], v[2][i], v[3][i], v[4][i], v[5][i], v[6][i], v[7][i], mult);
         if (staged) {
           lds_qt[(tx * 8 + i) * QT_STRIDE + ty] = w;

@@ -184,6 +184,9 @@ struct TileArgs {
   float* scale_inv_w;
   int margin;
   bool mx_ceil;
+  // MXFP8: a full tile's E8M0 bytes leave as one 4-byte store per row (s) and
+  // per column (st) when those runs are 4-byte aligned
+  bool s_vec, st_vec;
   int64_t tiles_c, ntiles;
 };
 
@@ -398,19 +401,44 @@ __global__ __launch_bounds__(256) void tile_kernel(TileArgs a) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) mm = umax(mm, umax(rowmax[k], colmax[k]));
         inrange = a.mx_ceil && mm < 0x7F800000u;
+        // E8M0 bytes of a full tile: through LDS (lds_red is free in this
+        // mode), row-block bytes [row][4], column-block bytes [col][4]
+        const bool tile_in = (r0 + TILE <= a.rows) && (c0 + TILE <= a.cols);
+        uint8_t* sbytes = reinterpret_cast<uint8_t*>(&lds_red[0][0]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           int e = mx_exponent(rowmax[j], EMAX, a.mx_ceil, a.margin);
           rs[j] = pow2_neg(e);
-          if (a.s && (tx & 3) == 0 && r + j < a.rows && c < a.cols)
-            reinterpret_cast<uint8_t*>(a.s)[(r + j) * (a.cols / 32) + (c >> 5)] = (uint8_t)(e + 127);
+          if (a.s && (tx & 3) == 0) {
+            if (tile_in && a.s_vec)
+              sbytes[(ty * 8 + j) * 4 + (tx >> 2)] = (uint8_t)(e + 127);
+            else if (r + j < a.rows && c < a.cols)
+              reinterpret_cast<uint8_t*>(a.s)[(r + j) * (a.cols / 32) + (c >> 5)] = (uint8_t)(e + 127);
+          }
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           int e = mx_exponent(canon(colmax[i]), EMAX, a.mx_ceil, a.margin);
           cs[i] = pow2_neg(e);
-          if (a.st && (ty & 3) == 0 && c + i < a.cols && r < a.rows)
-            reinterpret_cast<uint8_t*>(a.st)[(c + i) * (a.rows / 32) + (r >> 5)] = (uint8_t)(e + 127);
+          if (a.st && (ty & 3) == 0) {
+            if (tile_in && a.st_vec)
+              sbytes[512 + (tx * 8 + i) * 4 + (ty >> 2)] = (uint8_t)(e + 127);
+            else if (c + i < a.cols && r < a.rows)
+              reinterpret_cast<uint8_t*>(a.st)[(c + i) * (a.rows / 32) + (r >> 5)] = (uint8_t)(e + 127);
+          }
+        }
+        if (tile_in && ((a.s && a.s_vec) || (a.st && a.st_vec))) {
+          __syncthreads();
+          const uint32_t* w = reinterpret_cast<const uint32_t*>(sbytes);
+          if (tid < TILE) {
+            if (a.s && a.s_vec)
+              *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.s) + (r0 + tid) * (a.cols / 32) + c0 / 32) =
+                  w[tid];
+          } else if (a.st && a.st_vec) {
+            const int col = tid - TILE;
+            *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.st) + (c0 + col) * (a.rows / 32) + r0 / 32) =
+                w[TILE + col];
+          }
         }
       } else {
         // 1x128: row scale per row of the tile; 128x1: column scale needs all 4 waves
@@ -728,6 +756,8 @@ void launch_quantize_blocked(const void* x, int dtype, int64_t rows, int64_t col
   a.vec_ok = tile_vec_ok(x, dtype == 1 ? 2 : 4, rows, cols, ld, q, qt);
   a.q = q; a.qt = qt; a.s = q ? s : nullptr; a.st = qt ? st_ : nullptr;
   a.margin = margin; a.mx_ceil = mx_ceil;
+  a.s_vec = a.s && ((uintptr_t)a.s % 4 == 0) && (cols % 128 == 0);
+  a.st_vec = a.st && ((uintptr_t)a.st % 4 == 0) && (rows % 128 == 0);
   a.tiles_c = (cols + TILE - 1) / TILE;
   a.ntiles = ((rows + TILE - 1) / TILE) * a.tiles_c;
   if (scaling == 2)

@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(NvQuantArgs a) {
         uint32_t m = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) m = umax(m, absbits(v[j][i]));
-        m = umax(m, (uint32_t)__shfl_xor((int)m, 1, 64));
+        m = umax(m, dpp_u32<kDppXor1>(m));
         uint32_t code;
         float mult;
         block_scale(m > 0x7F800000u ? 0x7FC00000u : m, s_enc, lds_mult, code, mult);
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(NvQuantArgs a) {
         uint32_t m = 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) m = umax(m, absbits(v[j][i]));
-        m = umax(m, (uint32_t)__shfl_xor((int)m, 16, 64));
+        m = max_xor16(m);
         uint32_t code;
         float mult;
         block_scale(m > 0x7F800000u ? 0x7FC00000u : m, s_enc, lds_mult, code, mult);

@@ -125,27 +125,49 @@ __device__ __forceinline__ uint32_t abs_bits_canon(uint32_t u) {
 }
 
 // Wavefront (64 lanes) unsigned max via DPP/permute-free shuffles.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
-    v = v > o ? v : o;
+// Cross-lane moves without the LDS: DPP within a row of 16 lanes (quad
+// permutes, row rotates) and gfx950's v_permlane16/32_swap across rows.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1;   // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;   // quad_perm [2, 3, 0, 1]
+constexpr int kDppRor4 = 0x124;  // row_ror:4
+constexpr int kDppRor8 = 0x128;  // row_ror:8
+
+__device__ __forceinline__ uint32_t umax_u32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// max(v, v of lane l ^ 16): a swap of rows 1 and 0 (and 3 and 2) between two
+// copies of v leaves each lane holding its own value and its partner's
+__device__ __forceinline__ uint32_t max_xor16(uint32_t v) {
+  const auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return umax_u32(s[0], s[1]);
+}
+// max(v, v of lane l ^ 32), likewise with the two halves of the wave
+__device__ __forceinline__ uint32_t max_xor32(uint32_t v) {
+  const auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return umax_u32(s[0], s[1]);
+}
+
+// Max over lanes that differ only in the bits of MASK (xor pattern).  Bits 2
+// and 3 go together: max over lanes i + 0, 4, 8, 12 of a row by two rotates
+// is the max over i ^ {0, 4, 8, 12}.
+template <int MASK>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+  static_assert(((MASK >> 2) & 3) == 0 || ((MASK >> 2) & 3) == 3, "lane bits 2 and 3 are reduced together");
+  if constexpr (MASK & 1) v = umax_u32(v, dpp_u32<kDppXor1>(v));
+  if constexpr (MASK & 2) v = umax_u32(v, dpp_u32<kDppXor2>(v));
+  if constexpr (MASK & 4) {
+    v = umax_u32(v, dpp_u32<kDppRor4>(v));
+    v = umax_u32(v, dpp_u32<kDppRor8>(v));
   }
+  if constexpr (MASK & 16) v = max_xor16(v);
+  if constexpr (MASK & 32) v = max_xor32(v);
   return v;
 }
 
-// Max over lanes that differ only in the bits of MASK_BITS (xor pattern).
-template <int MASK>
-__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    if (MASK & off) {
-      uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
-      v = v > o ? v : o;
-    }
-  }
-  return v;
-}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return group_max_u32<0x3F>(v); }
 
 // Fold a workgroup's per-thread maxima (unsigned |x| bit patterns) into the
 // device-wide maximum at *out.  The workgroup reduces through LDS first and

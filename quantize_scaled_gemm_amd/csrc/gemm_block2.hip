@@ -22,9 +22,10 @@
 //     fragment reads per 2048 MFMA cycles per SIMD.
 //   * Operands go global -> LDS directly (buffer_load_dwordx4 ... lds) into
 //     two stages, with the swizzle of the 256 x 256 per-tensor kernel (16
-//     consecutive rows at one 16-byte chunk hit all 64 banks); the fetch of K
-//     tile t + 2 goes out once every wave is done reading tile t, and at the
-//     end of a tile it fetches the next tile's first K tiles.
+//     consecutive rows at one 16-byte chunk hit all 64 banks); one barrier
+//     per K tile, after which K tile t + 1 is fetched into the stage tile
+//     t - 1 used (the last K tile of an output tile fetches the next output
+//     tile's first).
 //   * Scales: 16 bytes per row (4 K blocks of fp32 scale_inv) per group of 4
 //     K tiles, one load instruction per wave, into two alternating group
 //     buffers, one group ahead.  Waves 0-3 fetch the 256 A rows' sa, waves
@@ -121,14 +122,6 @@ __device__ __forceinline__ void issue_tile(const Res& r, const uint32_t (&voa)[N
   for (int i = 0; i < NCK; ++i) dma16(r.rb, vob[i], kt * BK, st_b<S>() + i * NW * 1024 + wl);
 }
 
-// Load q (0 .. NCK-1) of the A tile and of the B tile of K tile kt.
-template <int S>
-__device__ __forceinline__ void issue_pair(const Res& r, const uint32_t (&voa)[NCK], const uint32_t (&vob)[NCK],
-                                           uint32_t wl, uint32_t kt, int q) {
-  dma16(r.ra, voa[q], kt * BK, st_a<S>() + q * NW * 1024 + wl);
-  dma16(r.rb, vob[q], kt * BK, st_b<S>() + q * NW * 1024 + wl);
-}
-
 // Scale group g: waves 0-3 the A rows' 16 bytes, waves 4-7 the B side's.
 template <int G>
 __device__ __forceinline__ void issue_group(const Res& r, uint32_t vos, uint32_t wl, uint32_t g) {
@@ -195,13 +188,10 @@ __global__ __launch_bounds__(NTH, 1) void gemm_block2_kernel(Block2Args g) {
   // B fragments are read PF fragments ahead of their MFMAs (the 1 x 128
   // layout holds 4 more scale factors per fragment and has no room for 2)
   constexpr int PF = W128 ? 2 : 1;
-  // Fetch schedule.  ONEBAR (1 x 128 layout): one barrier per K tile; the
-  // next K tile goes into the other stage during the first half of this one
-  // (two loads per fragment).  Otherwise two barriers per K tile: stage S is
-  // released once its last fragment is read and refilled at once with the K
-  // tile two ahead, which gives the loads more than a K tile to land (the
-  // weight-block fprop, whose output is the largest, loses 5 % without that).
-  constexpr bool ONEBAR = !W128;
+  // Fetch schedule: one barrier per K tile.  After it the other stage is
+  // free (every wave has read its fragments), and the first fragment's step
+  // fetches the next K tile into it; the wait before the barrier at the end
+  // of the K tile completes it.
   const int64_t sstride = (g.K / BK) * 4;   // bytes per scale row
 
   // fragment addressing
@@ -239,12 +229,7 @@ __global__ __launch_bounds__(NTH, 1) void gemm_block2_kernel(Block2Args g) {
   Res cur = resources(m0, n0);
   issue_group<0>(cur, vos, wl, 0);
   issue_tile<0>(cur, voa, vob, wl, 0);
-  if constexpr (ONEBAR) {
-    wait_vm_lgkm0<0>();  // group 0 and K tile 0 landed (this wave's part)
-  } else {
-    issue_tile<1>(cur, voa, vob, wl, 1);
-    wait_vm_lgkm0<2 * NCK>();
-  }
+  wait_vm_lgkm0<0>();  // group 0 and K tile 0 landed (this wave's part)
   lds_barrier();
 
   v4f acc[TI][TJ];
@@ -331,33 +316,13 @@ __global__ __launch_bounds__(NTH, 1) void gemm_block2_kernel(Block2Args g) {
       } else {                                                                                             \
         bf = bnn;                                                                                          \
       }                                                                                                    \
-      if constexpr (ONEBAR) {                                                                              \
-        if (j < NCK) {                                                                                     \
-          /* the next K tile into the other stage, one pair of loads per fragment */                        \
-          const bool own = (KT) + 1 < nk;                                                                  \
-          Res RES = own ? cur : nxt;                                                                       \
-          uint32_t FK = own ? (KT) + 1 : 0;                                                                \
-          asm volatile("" : "+s"(RES.ra), "+s"(RES.rb), "+s"(FK));                                         \
-          issue_pair<(S) ^ 1>(RES, voa, vob, wl, FK, j);                                                   \
-          if constexpr ((KI) == 1) {                                                                       \
-            if (j == 0) {                                                                                  \
-              const uint32_t ng = (KT) / GROUP + 1;                                                        \
-              const bool sown = ng < ngrp;                                                                 \
-              Res SR = sown ? cur : nxt;                                                                   \
-              uint32_t SG = sown ? ng : 0;                                                                 \
-              issue_group<(GB) ^ 1>(SR, vos, wl, SG);                                                      \
-            }                                                                                              \
-          }                                                                                                \
-        }                                                                                                  \
-      } else if (j == TJ - 1 - PF) {                                                                       \
-        /* every fragment of stage S is read: release it for K tile KT + 2 */                              \
-        wait_vm_lgkm0<63>();                                                                               \
-        lds_barrier();                                                                                     \
-        const bool own = (KT) + 2 < nk;                                                                    \
+      if (j == 0) {                                                                                        \
+        /* the next K tile into the other stage (free since the last barrier) */                           \
+        const bool own = (KT) + 1 < nk;                                                                    \
         Res RES = own ? cur : nxt;                                                                         \
-        uint32_t FK = own ? (KT) + 2 : (KT) + 2 - nk;                                                      \
+        uint32_t FK = own ? (KT) + 1 : 0;                                                                  \
         asm volatile("" : "+s"(RES.ra), "+s"(RES.rb), "+s"(FK));                                           \
-        issue_tile<S>(RES, voa, vob, wl, FK);                                                              \
+        issue_tile<(S) ^ 1>(RES, voa, vob, wl, FK);                                                        \
         if constexpr ((KI) == 1) {                                                                         \
           const uint32_t ng = (KT) / GROUP + 1;                                                            \
           const bool sown = ng < ngrp;                                                                     \
@@ -367,10 +332,7 @@ __global__ __launch_bounds__(NTH, 1) void gemm_block2_kernel(Block2Args g) {
         }                                                                                                  \
       }                                                                                                    \
     }                                                                                                      \
-    if constexpr (ONEBAR)                                                                                  \
-      wait_vm_lgkm0<0>();                                                                                  \
-    else                                                                                                   \
-      wait_vm_lgkm0<((KI) == 1 ? 2 * NCK + 1 : 2 * NCK)>();                                                \
+    wait_vm_lgkm0<0>();                                                                                    \
     lds_barrier();                                                                                         \
   }
 

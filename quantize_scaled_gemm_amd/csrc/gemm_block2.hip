@@ -63,7 +63,16 @@ struct Block2Args {
   int64_t tiles_m, tiles_n;
 };
 
-__device__ __forceinline__ int row_swizzle(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// 16-byte chunk c of LDS row r sits at position c ^ row_swizzle(r), with the
+// swizzle's bits 0, 1, 2 taken from row bits 1, 3, 2.  A fragment read
+// (lane l: row l % 16, chunk l / 16 or 4 + l / 16) then hits 16 distinct
+// 16-byte bank groups both within lanes 0-15 (all even or all odd rows get
+// all 8 swizzle values) and within lanes {8p .. 8p + 7} u {8p + 32 .. 8p + 39},
+// whose chunks differ by 2 (the 8 rows' swizzle values lie in distinct
+// classes {x, x ^ 2}).
+__device__ __forceinline__ int row_swizzle(int row) {
+  return ((row >> 1) & 1) | (((row >> 3) & 1) << 1) | (((row >> 2) & 1) << 2);
+}
 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
@@ -261,12 +270,12 @@ __global__ __launch_bounds__(NTH, 1) void gemm_block2_kernel(Block2Args g) {
     for (int v = 0; v < 4; ++v) pfb[v] = 0.0f;
 
     // K tile KT in stage S; its scales are word KI of group buffer GB.
-    //   1. scale factors and the 4 A fragments; the 8 B fragments one ahead
-    //      of their 4 MFMAs; the previous fragment's partial sums promoted
+    //   1. scale factors and the 4 A fragments; the B fragments PF ahead of
+    //      their 4 MFMAs; the previous fragment's partial sums promoted
     //      between them;
-    //   2. after the last fragment read: barrier, then the fetch of K tile
-    //      KT + 2 into S (and, at KI == 1, the next scale group);
-    //   3. wait for this wave's fetches of KT + 1, barrier.
+    //   2. in the first fragment's step, the fetch of K tile KT + 1 into
+    //      S ^ 1 (and, at KI == 1, of the next scale group);
+    //   3. wait for this wave's fetches, barrier.
 #define QSG_B2_STEP(S, KT, GB, KI)                                                                         \
   {                                                                                                        \
     float fa_[TI];                                                                                         \

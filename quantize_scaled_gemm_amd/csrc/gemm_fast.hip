@@ -24,7 +24,9 @@
 //     loop) instead of being issued in a burst, which would stall the
 //     in-order wave behind a full load queue.
 //   * MXFP8: the 4 E8M0 bytes of a row for the tile's 4 K blocks travel with
-//     the tile (buffer_load_dword ... lds); lane half h shifts its row's word by
+//     the tile (buffer_load_dword ... lds), or, where K allows, 16 bytes per
+//     row for groups of 4 K tiles, read into registers once per group (see
+//     GroupWords); lane half h shifts its row's word by
 //     8h so that op_sel 0 / 2 pick the bytes of K blocks h / 2+h for the two
 //     64-K MFMA steps (the MFMA operand K order: lane half h holds K
 //     [16h, 16h+16) and [32+16h, 48+16h) of a step; the scale of lanes 0..31
@@ -52,6 +54,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int FBM = 256, FBN = 256, FBK = 128;
@@ -73,11 +76,13 @@ struct FastArgs {
 };
 
 // 16-byte chunk c of LDS row r is stored at position c ^ row_swizzle(r).  A
-// fragment read has 16 lanes read 16 consecutive rows at one chunk; the LDS
-// serves a 16-lane group over 64 four-byte banks (256 B), and rows r and r+8
-// are 1 KB apart, i.e. on the same banks, so the swizzle flips bit 0 for the
-// second group of 8 rows: every 16-row group then covers all 64 banks, and
-// every 8-row group all 32 of the lower or upper half.
+// 128-byte row covers half of the 64 four-byte banks, so rows r and r + 2
+// share banks.  The LDS serves a 16-byte read for 16 lanes at a time, lanes
+// 8p .. 8p+7 together with 8p+32 .. 8p+39 [measured with the bank-conflict
+// counter]; in a fragment read those are rows 8p' .. 8p'+7 at chunk 2q
+// (lanes < 32) and 2q + 1, which the swizzle puts on 16 distinct 16-byte
+// bank groups.  (It also spreads any 16 consecutive rows at one chunk over
+// all 64 banks.)
 __device__ __forceinline__ int row_swizzle(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 
@@ -220,7 +225,7 @@ __device__ __forceinline__ void issue_stage(const TileRes& t, const uint32_t (&v
 
 // SC_MXG: the E8M0 bytes of scale group grp (K tiles 4 grp .. 4 grp + 3) of
 // the tile's 256 A rows and 256 B rows into group buffer GB: lane L of wave w
-// fetches the 16 bytes of row 64 w + L.
+// fills slot 64 w + L with the 16 bytes of row grp_slot(64 w + L) (`vos`).
 template <int GB>
 __device__ __forceinline__ void issue_scale_group(const TileRes& t, uint32_t vos, uint32_t wl, uint32_t grp) {
   dma16(t.rsa, vos, grp * 16, reinterpret_cast<uint8_t*>(group_sa<GB>()) + wl);
@@ -242,20 +247,53 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 
+// SC_MXG: the scale words of the current group, in registers.  The group
+// buffers hold row r in 16-byte slot grp_slot(r), which swaps bit 3 of the
+// row for rows with bit 5 set, so that one 16-byte read per lane of rows
+// base + 32 h + (l & 31) (lane half h) meets 16 distinct bank groups in every
+// set of lanes the LDS serves together (lanes 8p .. 8p+7 with 8p+32 .. 8p+39,
+// and 16 consecutive lanes).  a[p] / b[p] hold, in lane half h, the 4 words
+// (K tiles of the group) of row block 2p + h; a swap of the wave halves
+// (v_permlane32_swap) gives every lane the words of blocks 2p and 2p + 1.
+// (Reading one word per row and K tile instead puts rows r and r + 16 on one
+// bank: a 2-way conflict on every scale read.)
+__device__ __forceinline__ int grp_slot(int row) { return row ^ (((row >> 5) & 1) << 3); }
+
+template <int TN>
+struct GroupWords {
+  u32x4 a[TMW / 2], b[(TN + 1) / 2];
+};
+
 // Fragments of one 64-K step from stage S, and for MXFP8 the scale words of
 // the step's rows: from the stage's per-K-tile buffers (SC_MX) or word KI of
-// each row in group buffer GB (SC_MXG).
+// the group's words (SC_MXG; read from group buffer GB at KI == 0).
 template <int S, int SC, int GB, int KI, int TN>
-__device__ __forceinline__ void load_frags(Frags<TN>& f, int kk, int a_row_off, int b_row_off, int c_lo, int c_hi,
-                                           int a_srow, int b_srow, int sh) {
+__device__ __forceinline__ void load_frags(Frags<TN>& f, GroupWords<TN>& gw, int kk, int a_row_off, int b_row_off,
+                                           int c_lo, int c_hi, int a_srow, int b_srow, int a_gs, int b_gs, int sh) {
   if constexpr (SC == SC_MXG) {
     // step 0 only: the word shifted by 8h serves both 64-K steps (op_sel 0
     // and 2 pick bytes h and 2 + h); step 1 copies it (mfma_range<..., 2>)
     if (kk == 0) {
+      if constexpr (KI == 0) {
 #pragma unroll
-      for (int i = 0; i < TMW; ++i) f.sa[i] = (int)(group_sa<GB>()[(a_srow + i * 32) * 4 + KI] >> sh);
+        for (int p = 0; p < TMW / 2; ++p)
+          gw.a[p] = *reinterpret_cast<const u32x4*>(group_sa<GB>() + (a_gs + p * 64) * 4);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) f.sb[j] = (int)(group_sb<GB>()[(b_srow + j * 32) * 4 + KI] >> sh);
+        for (int p = 0; p < (TN + 1) / 2; ++p)
+          gw.b[p] = *reinterpret_cast<const u32x4*>(group_sb<GB>() + (b_gs + p * 64) * 4);
+      }
+#pragma unroll
+      for (int p = 0; p < TMW / 2; ++p) {
+        const auto w = __builtin_amdgcn_permlane32_swap(gw.a[p][KI], gw.a[p][KI], false, false);
+        f.sa[2 * p] = (int)(w[0] >> sh);
+        f.sa[2 * p + 1] = (int)(w[1] >> sh);
+      }
+#pragma unroll
+      for (int p = 0; p < (TN + 1) / 2; ++p) {
+        const auto w = __builtin_amdgcn_permlane32_swap(gw.b[p][KI], gw.b[p][KI], false, false);
+        f.sb[2 * p] = (int)(w[0] >> sh);
+        if (2 * p + 1 < TN) f.sb[2 * p + 1] = (int)(w[1] >> sh);
+      }
     }
   } else if constexpr (SC == SC_MX) {
 #pragma unroll
@@ -297,7 +335,6 @@ __device__ __forceinline__ void acc_read16(const v16f& a, float (&o)[16]) {
         : "a"(a[q]), "a"(a[q + 1]), "a"(a[q + 2]), "a"(a[q + 3]));
 }
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) uint8_t gbyte;
 
 // One 32 x 32 accumulator tile scaled by alpha and rearranged for 64-byte
@@ -502,6 +539,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
   const int c00 = ((0 + h) ^ x7) << 4, c01 = ((2 + h) ^ x7) << 4;
   const int c10 = ((4 + h) ^ x7) << 4, c11 = ((6 + h) ^ x7) << 4;
   const int a_srow = wm * WM + (lane & 31), b_srow = wn * WN + (lane & 31);
+  // SC_MXG: group-buffer slots of the rows of block h (lane half h)
+  const int a_gs = grp_slot(a_srow + 32 * h), b_gs = grp_slot(b_srow + 32 * h);
   // MX: bytes h (first 64-K step) and 2 + h (second) of the row's word
   const int sh0 = 8 * h, sh1 = 8 * h + 16;
   constexpr int OPS1 = SC == SC_MXG ? 2 : 0;  // scale byte of the second 64-K step
@@ -511,7 +550,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
   uint32_t voa[NCHUNK], vob[NCHUNK];
   chunk_offsets(voa, g.lda);
   chunk_offsets(vob, g.ldb);
-  const uint32_t vos = (uint32_t)(threadIdx.x * nb);
+  // scale row of this thread's fetch (SC_MXG: the row held by slot threadIdx.x)
+  const uint32_t vos = (uint32_t)((SC == SC_MXG ? grp_slot(threadIdx.x) : (int)threadIdx.x) * nb);
   const uint32_t wl = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
   auto resources = [&](uint32_t tm0, uint32_t tn0) {
     TileRes t;
@@ -538,7 +578,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
 
   v16f acc[TMW][TN];
   Frags<TN> f0, f1;
-  load_frags<0, SC, 0, 0, TN>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);
+  GroupWords<TN> gw;
+  load_frags<0, SC, 0, 0, TN>(f0, gw, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, a_gs, b_gs, sh0);
   while (true) {
     // The next tile's resources: the fetches of the last two K steps go to
     // its first two K tiles (or repeat this tile's, past the last tile), so
@@ -574,7 +615,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     pin_res<MX>(RES, FK);                                                                      \
     constexpr bool SGF = SC == SC_MXG && (KI) == 1;  /* this step fetches the next scale group */ \
     constexpr int NAS = NA + (SGF ? 2 : 0);                                                    \
-    load_frags<S, SC, GB, KI, TN>(f1, 1, a_row_off, b_row_off, c10, c11, a_srow, b_srow, sh1); \
+    load_frags<S, SC, GB, KI, TN>(f1, gw, 1, a_row_off, b_row_off, c10, c11, a_srow, b_srow, a_gs, b_gs, sh1); \
     if constexpr (SC == SC_MXG) {                                                              \
       _Pragma("unroll") for (int i = 0; i < TMW; ++i) f1.sa[i] = f0.sa[i];                     \
       _Pragma("unroll") for (int j = 0; j < TN; ++j) f1.sb[j] = f0.sb[j];                      \
@@ -610,7 +651,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     wait_vm_lgkm0<NAS>();                                                                      \
     lds_barrier();                                                                             \
     load_frags<S ^ 1, SC, ((KI) == 3 ? (GB) ^ 1 : (GB)), (((KI) + 1) & 3), TN>(                \
-        f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);                           \
+        f0, gw, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, a_gs, b_gs, sh0);          \
     issue_part<S, 1, SC, TN>(RES, voa, vob, vos, wl, FK);                                      \
     mfma_range<MX, FA, FB, P2, NQ, TN, OPS1>(acc, f1);                                         \
     _Pragma("unroll") for (int q = 0; q < NQ - P2 - 1; ++q) {                                  \
@@ -662,7 +703,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
     m0 = nm0;
     n0 = nn0;
     cur = nxt_t;
-    load_frags<0, SC, 0, 0, TN>(f0, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, sh0);
+    load_frags<0, SC, 0, 0, TN>(f0, gw, 0, a_row_off, b_row_off, c00, c01, a_srow, b_srow, a_gs, b_gs, sh0);
   }
 }
 

@@ -198,9 +198,9 @@ __global__ __launch_bounds__(NTH, 1) void gemm_block2_kernel(Block2Args g) {
   // layout holds 4 more scale factors per fragment and has no room for 2)
   constexpr int PF = W128 ? 2 : 1;
   // Fetch schedule: one barrier per K tile.  After it the other stage is
-  // free (every wave has read its fragments), and the first fragment's step
-  // fetches the next K tile into it; the wait before the barrier at the end
-  // of the K tile completes it.
+  // free (every wave has read its fragments), and the K tile's first
+  // instructions fetch the next K tile into it; the wait before the barrier
+  // at the end of the K tile completes it.
   const int64_t sstride = (g.K / BK) * 4;   // bytes per scale row
 
   // fragment addressing
@@ -270,14 +270,30 @@ __global__ __launch_bounds__(NTH, 1) void gemm_block2_kernel(Block2Args g) {
     for (int v = 0; v < 4; ++v) pfb[v] = 0.0f;
 
     // K tile KT in stage S; its scales are word KI of group buffer GB.
-    //   1. scale factors and the 4 A fragments; the B fragments PF ahead of
+    //   1. the fetch of K tile KT + 1 into S ^ 1 (and, at KI == 1, of the
+    //      next scale group), issued before any fragment read: issued after
+    //      them, the global -> LDS loads wait for every read in flight;
+    //   2. scale factors and the 4 A fragments; the B fragments PF ahead of
     //      their 4 MFMAs; the previous fragment's partial sums promoted
     //      between them;
-    //   2. in the first fragment's step, the fetch of K tile KT + 1 into
-    //      S ^ 1 (and, at KI == 1, of the next scale group);
     //   3. wait for this wave's fetches, barrier.
 #define QSG_B2_STEP(S, KT, GB, KI)                                                                         \
   {                                                                                                        \
+    {                                                                                                      \
+      /* the next K tile into the other stage (free since the last barrier) */                             \
+      const bool own = (KT) + 1 < nk;                                                                      \
+      Res RES = own ? cur : nxt;                                                                           \
+      uint32_t FK = own ? (KT) + 1 : 0;                                                                    \
+      asm volatile("" : "+s"(RES.ra), "+s"(RES.rb), "+s"(FK));                                             \
+      issue_tile<(S) ^ 1>(RES, voa, vob, wl, FK);                                                          \
+      if constexpr ((KI) == 1) {                                                                           \
+        const uint32_t ng = (KT) / GROUP + 1;                                                              \
+        const bool sown = ng < ngrp;                                                                       \
+        Res SR = sown ? cur : nxt;                                                                         \
+        uint32_t SG = sown ? ng : 0;                                                                       \
+        issue_group<(GB) ^ 1>(SR, vos, wl, SG);                                                            \
+      }                                                                                                    \
+    }                                                                                                      \
     float fa_[TI];                                                                                         \
     _Pragma("unroll") for (int i = 0; i < TI; ++i) fa_[i] = gr_sa<GB>()[sa_idx + i * 16 * GROUP + (KI)];   \
     float fb_w = 0.0f;                                                                                     \
@@ -286,7 +302,7 @@ __global__ __launch_bounds__(NTH, 1) void gemm_block2_kernel(Block2Args g) {
     _Pragma("unroll") for (int i = 0; i < TI; ++i) af[i] = frag16(st_a<S>(), a_off + i * 16 * BK, c_lo, c_hi); \
     v8i bf = frag16(st_b<S>(), b_off, c_lo, c_hi);                                                         \
     v8i bn = bf;                                                                                           \
-    if constexpr (PF == 2) bn = frag16(st_b<S>(), b_off + 16 * BK, c_lo, c_hi);                             \
+    if constexpr (PF == 2) bn = frag16(st_b<S>(), b_off + 16 * BK, c_lo, c_hi);                            \
     _Pragma("unroll") for (int j = 0; j < TJ; ++j) {                                                       \
       v8i bnn = bn;                                                                                        \
       if (j + PF < TJ) bnn = frag16(st_b<S>(), b_off + (j + PF) * 16 * BK, c_lo, c_hi);                    \
@@ -324,21 +340,6 @@ __global__ __launch_bounds__(NTH, 1) void gemm_block2_kernel(Block2Args g) {
         bn = bnn;                                                                                          \
       } else {                                                                                             \
         bf = bnn;                                                                                          \
-      }                                                                                                    \
-      if (j == 0) {                                                                                        \
-        /* the next K tile into the other stage (free since the last barrier) */                           \
-        const bool own = (KT) + 1 < nk;                                                                    \
-        Res RES = own ? cur : nxt;                                                                         \
-        uint32_t FK = own ? (KT) + 1 : 0;                                                                  \
-        asm volatile("" : "+s"(RES.ra), "+s"(RES.rb), "+s"(FK));                                           \
-        issue_tile<(S) ^ 1>(RES, voa, vob, wl, FK);                                                        \
-        if constexpr ((KI) == 1) {                                                                         \
-          const uint32_t ng = (KT) / GROUP + 1;                                                            \
-          const bool sown = ng < ngrp;                                                                     \
-          Res SR = sown ? cur : nxt;                                                                       \
-          uint32_t SG = sown ? ng : 0;                                                                     \
-          issue_group<(GB) ^ 1>(SR, vos, wl, SG);                                                          \
-        }                                                                                                  \
       }                                                                                                    \
     }                                                                                                      \
     wait_vm_lgkm0<0>();                                                                                    \

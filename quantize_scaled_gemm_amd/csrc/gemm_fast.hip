@@ -71,6 +71,7 @@ struct FastArgs {
   bool accumulate;  // fp32 C only: C = fp32(C + result)
   int64_t tiles_m, tiles_n;
   int64_t max_wgs;  // persistent grid: one workgroup per CU
+  uint32_t gm;      // tile-rows per group of the tile order
   const float* ta;  // NVFP4: the operands' per-tensor decode scales
   const float* tb;
 };
@@ -393,10 +394,10 @@ __device__ __forceinline__ void tile_pieces(const v16f& acc, float alpha, u32x4 
 
 // Tile t of the XCD-aware order: workgroup ids are dispatched round-robin
 // over the 8 XCDs, each XCD owns a contiguous range of the logical tile
-// order, walked in groups of 4 tile-rows x all tile-columns.
+// order, walked in groups of g.gm tile-rows x all tile-columns.
 template <int TN>
 __device__ __forceinline__ void tile_coords(const FastArgs& g, uint32_t logical, uint32_t& m0, uint32_t& n0) {
-  constexpr uint32_t GM = 4;
+  const uint32_t GM = g.gm;
   const uint32_t tm = (uint32_t)g.tiles_m, tn = (uint32_t)g.tiles_n;
   const uint32_t per_group = GM * tn;
   const uint32_t first_m = (logical / per_group) * GM;
@@ -958,6 +959,14 @@ int device_cu_count() {
   return cached[dev];
 }
 
+// Tile-rows per group of the tile order.  The 32 tiles an XCD runs at once
+// span gm tile-rows x 32 / gm tile-columns; 4 and 8 read the same panels per
+// tile.  [measured, same-box A/Bs on two boxes] 8 is 1-3 % faster than 4
+// where K is short and the output narrow (32768 x 4096 x 4096 fprop and
+// dgrad) and 3-4 % slower on the long-K 32768 x 4096 x 14336 dgrad; 4
+// elsewhere.
+uint32_t tile_group_rows(int64_t K, int64_t tiles_n) { return (K <= 4096 && tiles_n <= 16) ? 8u : 4u; }
+
 template <int SC, int FA, int FB>
 void launch_fast_cfg(const FastArgs& g, bool out_bf16, int tn, hipStream_t st) {
   const int64_t tiles = g.tiles_m * g.tiles_n;
@@ -1006,6 +1015,7 @@ bool launch_scaled_gemm_fast(const uint8_t* a, int fa, bool mx, const void* sa, 
   g.tiles_m = tiles_m;
   g.tiles_n = tiles_n;
   g.max_wgs = device_cu_count();
+  g.gm = tile_group_rows(K, tiles_n);
   // MXFP8 scale bytes in groups of 4 K tiles when whole pairs of groups fit
   // every tile's K (16-byte aligned rows of scale bytes)
   const bool mx_grouped = mx && K % (8 * FBK) == 0;
@@ -1064,6 +1074,7 @@ bool launch_gemm_nvfp4_fast(const uint8_t* a, const uint8_t* sa, const float* ta
   g.tiles_m = tiles_m;
   g.tiles_n = tiles_n;
   g.max_wgs = device_cu_count();
+  g.gm = 4;
   const int64_t tiles = tiles_m * tiles_n;
   const unsigned grid = (unsigned)(tiles < g.max_wgs ? tiles : g.max_wgs);
   if (out_bf16)

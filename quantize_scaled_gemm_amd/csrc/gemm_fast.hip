@@ -33,13 +33,13 @@
 //     covers K 0..31 and that of lanes 32..63 covers K 32..63).
 //   * Persistent workgroups, one per CU.  Workgroup ids are dispatched
 //     round-robin over the 8 XCDs; the workgroups of an XCD take turns over a
-//     contiguous range of the tile order, walked in groups of 4 tile-rows x
-//     all tile-columns, so the 32 tiles an XCD runs at once share 4 A panels
-//     and 8 B panels in its L2.  The operand stream runs across tile
-//     boundaries: the last two K steps of a tile fetch the next tile's first
-//     two K tiles, and the results are stored straight from registers
-//     without waiting for any fetch, so the next tile starts on operands
-//     that are already in LDS.
+//     contiguous range of the tile order, walked in groups of 4 (or 8, see
+//     tile_group_rows) tile-rows x all tile-columns, so the 32 tiles an XCD
+//     runs at once share 4 A panels and 8 B panels (8 and 4) in its L2.  The
+//     operand stream runs across tile boundaries: the last two K steps of a
+//     tile fetch the next tile's first two K tiles, and the results are
+//     stored straight from registers without waiting for any fetch, so the
+//     next tile starts on operands that are already in LDS.
 //   * A last round of tiles that would leave at least half the CUs idle runs
 //     as a second launch of 256 x 128 tiles (each wave 128 x 64), twice as
 //     many work items of half the size.

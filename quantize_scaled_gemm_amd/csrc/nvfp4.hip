@@ -434,7 +434,7 @@ void launch_quantize_nvfp4(const void* x, int dtype, int64_t rows, int64_t cols,
   a.st_vec = st && ((uintptr_t)st % 8 == 0) && (rows % 128 == 0);
   a.tiles_c = (cols + 127) / 128;
   a.ntiles = ((rows + 127) / 128) * a.tiles_c;
-  int64_t grid = a.ntiles, cap = (int64_t)nv_num_cus() * 8;
+  int64_t grid = a.ntiles, cap = (int64_t)nv_num_cus() * 128;  // one tile per workgroup up to 128 per CU
   if (grid > cap) grid = cap;
   if (dtype == 1)
     hipLaunchKernelGGL(nvfp4_quant_kernel<uint16_t>, dim3((unsigned)grid), dim3(256), 0, stream, a);

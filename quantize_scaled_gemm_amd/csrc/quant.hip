@@ -596,10 +596,11 @@ int num_cus() {
 
 template <typename In, int MODE>
 void launch_tile(const TileArgs& a, int fmt, hipStream_t st) {
-  // With a fused amax the per-tensor cast runs a persistent grid of 2
-  // workgroups per CU: the amax ends in one device-scope atomic per workgroup
-  // on one address, which the memory side performs one at a time (with 8 per
-  // CU a 64 MB tensor spent more time on them than on its bytes).  Without
+  // With a fused amax (or the delayed step's amax and history update) the
+  // per-tensor cast runs a persistent grid of 2 workgroups per CU: the amax
+  // ends in one device-scope atomic per workgroup on one address, which the
+  // memory side performs one at a time (with 8 per CU a 64 MB tensor spent
+  // more time on them than on its bytes).  Without
   // atomics every mode runs one tile per workgroup up to 128 per CU
   // (grid-stride beyond): [measured, same-box A/Bs against a persistent grid]
   // per-tensor cast X 32768 x 4096 +4 %, dY2 32768 x 14336 +3 %, W 4096 x
@@ -607,7 +608,8 @@ void launch_tile(const TileArgs& a, int fmt, hipStream_t st) {
   // 16384 x 7168 / dY 16384 x 18432 +6 / +8 %, 128 x 128 W 18432 x 7168
   // +3-4 %, MXFP8 X and W (16384 / 14336 x 4096) +0-2 % (against 8 per CU).
   int64_t grid = a.ntiles;
-  const int64_t cap = (int64_t)num_cus() * ((MODE == MODE_TENSOR && a.amax_out) ? 2 : 128);
+  const bool atomics = MODE == MODE_TENSOR && (a.amax_out || a.ws);
+  const int64_t cap = (int64_t)num_cus() * (atomics ? 2 : 128);
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
   if (fmt == kE4M3)

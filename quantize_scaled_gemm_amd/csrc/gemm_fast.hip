@@ -723,7 +723,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(FastArgs g) {
 //   * The same 256 x 256 workgroup tile, waves and LDS stages as the FP8
 //     kernel: a K tile is 256 elements = 128 bytes of codes per row, fetched
 //     global -> LDS with the FP8 chunk mapping and swizzle; the tile's 16
-//     scale bytes per row travel to the group buffers (16 B per row).
+//     scale bytes per row travel to the group buffers (16 B per row, in the
+//     slot order of GroupWords) and are read into registers once per K tile.
 //   * Each wave decodes its own fragments from LDS.  For a 64-K chunk of a
 //     K tile, lane half h reads the 16 bytes (32 codes) of K [32h, 32h + 32)
 //     of its row with one ds_read_b128; step s = 0..3 of the chunk feeds
@@ -762,19 +763,41 @@ struct NvChunk {
   uint32_t sa[TMW], sb[4];
 };
 
+// Per-lane addressing of the NVFP4 kernel.
+struct NvAddr {
+  int slot[4];  // swizzled byte offset of chunk c's 16 bytes for this lane half
+  int a_row_off, b_row_off, sh;
+  int a_gs, b_gs;  // group-buffer slots of the rows of block h (lane half h)
+};
+
+// The row scale words of chunk c (0..3) come from the K tile's 16 scale bytes
+// per row, read into gw at chunk 0 (two 16-byte reads per operand: lane half h
+// takes row block 2p + h, from the bank-spread slot order of GroupWords) and
+// exchanged between the wave halves per chunk.
 template <int S>
-__device__ __forceinline__ void nv_read_chunk(NvChunk& r, int c, int slot, int a_row_off, int b_row_off, int a_srow,
-                                              int b_srow, int sh) {
+__device__ __forceinline__ void nv_read_chunk(NvChunk& r, GroupWords<4>& gw, int c, int slot, const NvAddr& ad) {
 #pragma unroll
   for (int i = 0; i < TMW; ++i)
-    r.a[i] = *reinterpret_cast<const u32x4*>(stage_a<S>() + a_row_off + i * 32 * FBK + slot);
+    r.a[i] = *reinterpret_cast<const u32x4*>(stage_a<S>() + ad.a_row_off + i * 32 * FBK + slot);
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    r.b[j] = *reinterpret_cast<const u32x4*>(stage_b<S>() + b_row_off + j * 32 * FBK + slot);
+    r.b[j] = *reinterpret_cast<const u32x4*>(stage_b<S>() + ad.b_row_off + j * 32 * FBK + slot);
+  if (c == 0) {
 #pragma unroll
-  for (int i = 0; i < TMW; ++i) r.sa[i] = group_sa<S>()[(a_srow + i * 32) * 4 + c] >> sh;
+    for (int p = 0; p < 2; ++p) {
+      gw.a[p] = *reinterpret_cast<const u32x4*>(group_sa<S>() + (ad.a_gs + p * 64) * 4);
+      gw.b[p] = *reinterpret_cast<const u32x4*>(group_sb<S>() + (ad.b_gs + p * 64) * 4);
+    }
+  }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) r.sb[j] = group_sb<S>()[(b_srow + j * 32) * 4 + c] >> sh;
+  for (int p = 0; p < 2; ++p) {
+    const auto wa = __builtin_amdgcn_permlane32_swap(gw.a[p][c], gw.a[p][c], false, false);
+    r.sa[2 * p] = wa[0] >> ad.sh;
+    r.sa[2 * p + 1] = wa[1] >> ad.sh;
+    const auto wb = __builtin_amdgcn_permlane32_swap(gw.b[p][c], gw.b[p][c], false, false);
+    r.sb[2 * p] = wb[0] >> ad.sh;
+    r.sb[2 * p + 1] = wb[1] >> ad.sh;
+  }
 }
 
 // Fragments of step s (0..3) of a chunk.
@@ -806,31 +829,25 @@ __device__ __forceinline__ void nv_issue(const TileRes& t, const uint32_t (&voa)
   dma16(t.rsb, vos, kt * 16, reinterpret_cast<uint8_t*>(group_sb<S>()) + wl);
 }
 
-// Per-lane addressing of the NVFP4 kernel.
-struct NvAddr {
-  int slot[4];  // swizzled byte offset of chunk c's 16 bytes for this lane half
-  int a_row_off, b_row_off, a_srow, b_srow, sh;
-};
-
 // One K tile in stage S.  On entry r0 holds its first chunk and (fa, fb) the
 // fragments of its first step; on return r0 holds the next K tile's first
 // chunk (stage S ^ 1) and (fa, fb) that K tile's first-step fragments.  At
 // step 12 the stage is refilled with K tile fk of `res`.
 template <int S>
-__device__ __forceinline__ void nv_ktile(v16f (&acc)[TMW][4], NvChunk& r0, nv_h8 (&fa)[TMW], nv_h8 (&fb)[4],
-                                         const NvAddr& ad, TileRes res, uint32_t fk, const uint32_t (&voa)[NCHUNK],
+__device__ __forceinline__ void nv_ktile(v16f (&acc)[TMW][4], NvChunk& r0, GroupWords<4>& gw, nv_h8 (&fa)[TMW],
+                                         nv_h8 (&fb)[4], const NvAddr& ad, TileRes res, uint32_t fk, const uint32_t (&voa)[NCHUNK],
                                          const uint32_t (&vob)[NCHUNK], uint32_t vos, uint32_t wl) {
   NvChunk rc = r0, rn;
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
     const int c = t / 4, s = t % 4;
-    if (s == 1 && c < 3) nv_read_chunk<S>(rn, c + 1, ad.slot[c + 1], ad.a_row_off, ad.b_row_off, ad.a_srow, ad.b_srow, ad.sh);
+    if (s == 1 && c < 3) nv_read_chunk<S>(rn, gw, c + 1, ad.slot[c + 1], ad);
     if (t == 12) {
       pin_res<true>(res, fk);
       wait_vm_lgkm0<0>();
       lds_barrier();
       nv_issue<S>(res, voa, vob, vos, wl, fk);
-      nv_read_chunk<S ^ 1>(r0, 0, ad.slot[0], ad.a_row_off, ad.b_row_off, ad.a_srow, ad.b_srow, ad.sh);
+      nv_read_chunk<S ^ 1>(r0, gw, 0, ad.slot[0], ad);
     }
     nv_h8 na[TMW], nb[4];
     if (t < 15)
@@ -881,15 +898,15 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_fast_kernel(FastArgs g) {
   for (int c = 0; c < 4; ++c) ad.slot[c] = ((2 * c + h) ^ x7) << 4;
   ad.a_row_off = (wm * WM + (lane & 31)) * FBK;
   ad.b_row_off = (wn * WN + (lane & 31)) * FBK;
-  ad.a_srow = wm * WM + (lane & 31);
-  ad.b_srow = wn * WN + (lane & 31);
+  ad.a_gs = grp_slot(wm * WM + 32 * h + (lane & 31));
+  ad.b_gs = grp_slot(wn * WN + 32 * h + (lane & 31));
   ad.sh = 16 * h;
   const float alpha = *g.ta * *g.tb;
 
   uint32_t voa[NCHUNK], vob[NCHUNK];
   chunk_offsets(voa, g.lda);
   chunk_offsets(vob, g.ldb);
-  const uint32_t vos = (uint32_t)(threadIdx.x * nsb);
+  const uint32_t vos = (uint32_t)(grp_slot(threadIdx.x) * nsb);  // the row held by slot threadIdx.x
   const uint32_t wl = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
   auto resources = [&](uint32_t tm0, uint32_t tn0) {
     TileRes t;
@@ -910,8 +927,9 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_fast_kernel(FastArgs g) {
 
   v16f acc[TMW][TN];
   NvChunk r0;
+  GroupWords<4> gw;
   nv_h8 fa[TMW], fb[TN];
-  nv_read_chunk<0>(r0, 0, ad.slot[0], ad.a_row_off, ad.b_row_off, ad.a_srow, ad.b_srow, ad.sh);
+  nv_read_chunk<0>(r0, gw, 0, ad.slot[0], ad);
   nv_frags(r0, 0, fa, fb);
   while (true) {
     const int64_t cm0 = m0, cn0 = n0;
@@ -931,8 +949,8 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_fast_kernel(FastArgs g) {
     // first or second (or this tile's again after the last tile)
     uint32_t kt = 0;
     do {
-      nv_ktile<0>(acc, r0, fa, fb, ad, kt + 2 < nk ? cur : nxt_t, kt + 2 < nk ? kt + 2 : kt + 2 - nk, voa, vob, vos, wl);
-      nv_ktile<1>(acc, r0, fa, fb, ad, kt + 3 < nk ? cur : nxt_t, kt + 3 < nk ? kt + 3 : kt + 3 - nk, voa, vob, vos, wl);
+      nv_ktile<0>(acc, r0, gw, fa, fb, ad, kt + 2 < nk ? cur : nxt_t, kt + 2 < nk ? kt + 2 : kt + 2 - nk, voa, vob, vos, wl);
+      nv_ktile<1>(acc, r0, gw, fa, fb, ad, kt + 3 < nk ? cur : nxt_t, kt + 3 < nk ? kt + 3 : kt + 3 - nk, voa, vob, vos, wl);
       kt += 2;
     } while (kt < nk);
     store_tile<OUT_BF16, TN>(g, acc, alpha, cm0, cn0, wm, wn, lane);

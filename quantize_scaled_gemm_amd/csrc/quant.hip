@@ -23,8 +23,10 @@
 //     blocks are the 4 row-groups of one wave (xor 16, 32); 1x128 row blocks
 //     are 16 lanes; 128x1 column blocks and 128x128 blocks reduce across the
 //     4 waves through LDS.
-// The grid is persistent (grid-stride over tiles, row-major tile order), so
-// the fused amax of the per-tensor path costs one atomic per workgroup.
+// The kernel walks the tiles in row-major order with a grid stride: a
+// persistent grid of 2 workgroups per CU where the per-tensor path fuses the
+// amax (one atomic per workgroup), otherwise one tile per workgroup (see
+// launch_tile).
 #include <hip/hip_runtime.h>
 
 #include <mutex>

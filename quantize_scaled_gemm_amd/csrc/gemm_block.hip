@@ -217,7 +217,9 @@ __device__ __forceinline__ void mfma_seq(v16f (&acc)[TMW][TNW], v16f (&part)[TMW
 
 template <int FA, int FB, bool OUT_BF16>
 __global__ __launch_bounds__(256, 2) void gemm_block_kernel(BlockArgs g) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index in an SGPR: the per-wave offsets derived from it then need
+  // no VGPR held across the K loop
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   // tile coordinates: XCD-contiguous ranges, groups of 4 tile-rows

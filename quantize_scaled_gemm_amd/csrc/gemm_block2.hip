@@ -21,11 +21,10 @@
 //     accumulator VGPRs.  A K tile costs 64 KB of operand fetch and 192 KB of
 //     fragment reads per 2048 MFMA cycles per SIMD.
 //   * Operands go global -> LDS directly (buffer_load_dwordx4 ... lds) into
-//     two stages, with the swizzle of the 256 x 256 per-tensor kernel (16
-//     consecutive rows at one 16-byte chunk hit all 64 banks); one barrier
-//     per K tile, after which K tile t + 1 is fetched into the stage tile
-//     t - 1 used (the last K tile of an output tile fetches the next output
-//     tile's first).
+//     two stages, with a row swizzle that keeps the 16 x 16 x 128 fragment
+//     reads free of bank conflicts (see row_swizzle); one barrier per K tile,
+//     after which K tile t + 1 is fetched into the stage tile t - 1 used (the
+//     last K tile of an output tile fetches the next output tile's first).
 //   * Scales: 16 bytes per row (4 K blocks of fp32 scale_inv) per group of 4
 //     K tiles, one load instruction per wave, into two alternating group
 //     buffers, one group ahead.  Waves 0-3 fetch the 256 A rows' sa, waves
